@@ -1,0 +1,210 @@
+"""CPU oracle for fine-grained FP8 quantization and the block-scaled FP8 GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library never
+calls it, and it never calls the HIP library; the two share no code.
+
+The arithmetic lives in ``fp8q_oracle.c`` (plain C, fp32 steps exactly as IEEE
+binary32, the GEMM in double).  This module only compiles that file with gcc,
+loads it with ctypes and marshals numpy arrays.  Every function states which
+part of the method it follows; the citations are in the C file's header.
+
+Array conventions (numpy, C-contiguous):
+  * bf16 tensors are ``uint16`` bit patterns;
+  * FP8 tensors are ``uint8`` OCP E4M3 codes;
+  * activation scales ``s_a`` have shape ``[K/128, M]`` (K-block-major);
+  * weight scales ``s_w`` have shape ``[N/128, K/128]`` (per expert for MoE).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8q_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_fp8q.so")
+_lock = threading.Lock()
+_lib = None
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc.  Returns the path of the shared library."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library and declare its C signatures."""
+    global _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        p = path or _LIB_PATH
+        if not os.path.exists(p) or (path is None and os.path.getmtime(p) < os.path.getmtime(_SRC)):
+            build(out=p)
+        lib = ctypes.CDLL(p)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
+        lib.oracle_e4m3_encode_array.restype = None
+        lib.oracle_quant_act_1x128.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_act_1x128.restype = ctypes.c_int
+        lib.oracle_quant_w_128x128.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_w_128x128.restype = ctypes.c_int
+        lib.oracle_gemm_blockscaled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P, P]
+        lib.oracle_gemm_blockscaled.restype = ctypes.c_int
+        lib.oracle_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I64, P, P]
+        lib.oracle_grouped_gemm_blockscaled.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str):
+    if rc == -1:
+        raise ValueError(f"{what}: bad shape or index")
+    if rc == -2:
+        raise ValueError(f"{what}: non-finite input (finite input is a precondition)")
+    if rc != 0:
+        raise RuntimeError(f"{what}: status {rc}")
+
+
+# ---------------------------------------------------------------------------
+# OCP E4M3 code <-> value
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes, lib=None) -> np.ndarray:
+    """float64 value of each E4M3 code (NaN for 0x7F / 0xFF)."""
+    lib = lib or load()
+    table = np.array([lib.oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(values, lib=None) -> np.ndarray:
+    """E4M3 code of each fp32 value: nearest, ties to even, saturating at 448."""
+    lib = lib or load()
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib.oracle_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Quantizers
+# ---------------------------------------------------------------------------
+
+def quant_act_1x128(x_bits, lib=None):
+    """1x128 activation quantization of bf16 ``x [M, K]``.
+
+    Returns ``(q uint8 [M, K], s_a float32 [K/128, M])``.
+    """
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((K // 128, M), dtype=np.float32)
+    _check(lib.oracle_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s)), "quant_act_1x128")
+    return q, s
+
+
+def quant_w_128x128(w_bits, lib=None):
+    """128x128 weight quantization of bf16 ``w [N, K]`` (or ``[E, N, K]``, one block grid per expert).
+
+    Returns ``(q uint8, s_w float32 [N/128, K/128])`` (``[E, N/128, K/128]`` for 3-D input).
+    """
+    lib = lib or load()
+    w = _c(w_bits, np.uint16)
+    lead = w.shape[:-2]
+    N, K = w.shape[-2:]
+    rows = int(np.prod(lead, dtype=np.int64)) * N if lead else N
+    q = np.empty(w.shape, dtype=np.uint8)
+    s = np.empty(lead + (N // 128, K // 128), dtype=np.float32)
+    # An [E, N, K] stack with N % 128 == 0 is the same block grid as one [E*N, K] matrix.
+    _check(lib.oracle_quant_w_128x128(_ptr(w), rows, K, _ptr(q), _ptr(s)), "quant_w_128x128")
+    return q, s
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def _elements(M, N, rows, cols):
+    if rows is None and cols is None:
+        ms = np.repeat(np.arange(M, dtype=np.int64), N)
+        ns = np.tile(np.arange(N, dtype=np.int64), M)
+        return ms, ns, (M, N)
+    if rows is not None and cols is None:
+        rows = np.asarray(rows, dtype=np.int64)
+        return np.repeat(rows, N), np.tile(np.arange(N, dtype=np.int64), len(rows)), (len(rows), N)
+    if rows is None:
+        cols = np.asarray(cols, dtype=np.int64)
+        return np.repeat(np.arange(M, dtype=np.int64), len(cols)), np.tile(cols, M), (M, len(cols))
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    return np.repeat(rows, len(cols)), np.tile(cols, len(rows)), (len(rows), len(cols))
+
+
+def gemm_blockscaled(qa, sa, qw, sw, rows=None, cols=None, lib=None):
+    """Dequantized GEMM ``C = A_deq @ W_deq^T`` in float64, with the error scale ``B = |A_deq| @ |W_deq|^T``.
+
+    ``rows``/``cols`` select a sub-grid of output elements (all rows / all columns when None).
+    Returns ``(C, B)`` as float64 arrays of shape ``[len(rows) or M, len(cols) or N]``.
+    """
+    lib = lib or load()
+    qa = _c(qa, np.uint8)
+    qw = _c(qw, np.uint8)
+    sa = _c(sa, np.float32)
+    sw = _c(sw, np.float32)
+    M, K = qa.shape
+    N = qw.shape[0]
+    assert qw.shape == (N, K) and sa.shape == (K // 128, M) and sw.shape == (N // 128, K // 128)
+    ms, ns, shape = _elements(M, N, rows, cols)
+    C = np.empty(ms.shape, dtype=np.float64)
+    B = np.empty(ms.shape, dtype=np.float64)
+    _check(lib.oracle_gemm_blockscaled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, _ptr(ms), _ptr(ns),
+                                       len(ms), _ptr(C), _ptr(B)), "gemm_blockscaled")
+    return C.reshape(shape), B.reshape(shape)
+
+
+def grouped_gemm_blockscaled(qa, sa, qw, sw, offsets, rows=None, cols=None, lib=None):
+    """Grouped (MoE) dequantized GEMM: rows ``[off[e], off[e+1])`` of A use expert ``e``.
+
+    ``qw [E, N, K]``, ``sw [E, N/128, K/128]``, ``offsets int32 [E+1]``.  Returns ``(C, B)`` like
+    :func:`gemm_blockscaled`.
+    """
+    lib = lib or load()
+    qa = _c(qa, np.uint8)
+    qw = _c(qw, np.uint8)
+    sa = _c(sa, np.float32)
+    sw = _c(sw, np.float32)
+    off = _c(offsets, np.int32)
+    M, K = qa.shape
+    E, N, K2 = qw.shape
+    assert K2 == K and sa.shape == (K // 128, M) and sw.shape == (E, N // 128, K // 128) and off.shape == (E + 1,)
+    ms, ns, shape = _elements(M, N, rows, cols)
+    C = np.empty(ms.shape, dtype=np.float64)
+    B = np.empty(ms.shape, dtype=np.float64)
+    _check(lib.oracle_grouped_gemm_blockscaled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(off), E, M, N, K,
+                                               _ptr(ms), _ptr(ns), len(ms), _ptr(C), _ptr(B)),
+           "grouped_gemm_blockscaled")
+    return C.reshape(shape), B.reshape(shape)

@@ -1,0 +1,239 @@
+/*
+ * fp8q_oracle.c -- plain, slow CPU oracle for fine-grained FP8 quantization and
+ * the block-scaled FP8 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file: it exists so that tests/, the smoke check and the benchmark's CPU
+ * baseline can check the HIP library against an independent definition.  It
+ * shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes, and where that comes from:
+ *
+ *  - Grouping (page "The Definitive Information To Deepseek", the passage that
+ *    refers to Figure 7 (a)): activations are grouped and scaled per 1x128 tile
+ *    (one token, 128 consecutive channels); weights per 128x128 block (128
+ *    output channels x 128 input channels).
+ *  - Online scaling (same page, the passage on caching the Linear operator's
+ *    input in FP8 for the backward pass): a scaling factor is derived per group
+ *    and the group is then quantized to FP8 online.  The page lost what the
+ *    factor is derived from; the reading taken here is the group's maximum
+ *    absolute value, with scale = fl32(amax / 448), 448 being the largest
+ *    finite E4M3 magnitude.
+ *  - FP8 flavour: OCP 8-bit floating point E4M3 ("FN": bias 7, no infinities,
+ *    S.1111.111 is NaN, largest finite 448, subnormals m * 2^-9).
+ *  - Encoding: v = fl32(x / scale), then round to the nearest E4M3 value with
+ *    ties to even, saturating at +-448, keeping the sign (so -0 -> 0x80).  The
+ *    rounding x/s -> fp32 -> E4M3 is a double rounding on purpose: it is the
+ *    definition the GPU path must reproduce bit for bit.
+ *  - GEMM (same page, the passage stating that the GEMMs take FP8 inputs and
+ *    produce BF16 or FP32 outputs, and the passage on promotion overlapping the
+ *    MMA on H800 warpgroups): the product C = A * W^T of the dequantized
+ *    operands, where every element is its E4M3 value times its group's scale.
+ *    This oracle evaluates that sum in double precision, with the error scale
+ *    B = sum_k |a_deq[m,k]| * |w_deq[n,k]|.  Promotion of partial sums at every
+ *    128-element K interval is how a GPU reaches this value in fp32; the
+ *    oracle does not model it, it computes the value itself.
+ *
+ * Layouts (a reading; the pages are silent): row-major, K contiguous.
+ * Activation scales s_a are stored K-block-major, s_a[kb * M + m]; weight scales
+ * s_w[nb * KB + kb] with nb = n / 128 and KB = K / 128.
+ *
+ * Precision: compiled without -ffast-math and with -ffp-contract=off, on an
+ * x86-64 target where float expressions are evaluated in float, so every fp32
+ * operation written here is one IEEE-754 binary32 operation.
+ *
+ * Pins: tests/test_oracle_*.py check this file against hand-worked E4M3 cases,
+ * the OCP closed-form code table, a brute-force nearest-value encoder over all
+ * bf16 inputs, sign/scale invariants, a lossless special case equal to a
+ * float64 numpy matmul, and exact rational sums on tiny shapes.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle requires float expressions to be evaluated in float"
+#endif
+
+#define GROUP 128
+
+/* ---- bf16 ---------------------------------------------------------------- */
+
+/* A bf16 value is the upper half of an fp32 bit pattern: widening is exact. */
+static float bf16_to_f32(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ---- OCP E4M3 -------------------------------------------------------------- */
+
+/* Magnitude of a non-negative finite code 0x00..0x7E, straight from the format:
+ * exponent field e (bias 7) and mantissa field m (3 bits);
+ * e == 0: subnormal m/8 * 2^-6 = m * 2^-9;  e >= 1: (1 + m/8) * 2^(e-7). */
+static double e4m3_magnitude(unsigned code) {
+    unsigned e = (code >> 3) & 0xFu, m = code & 0x7u;
+    if (e == 0) return ldexp((double)m, -9);
+    return ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+}
+
+double oracle_e4m3_decode(uint8_t code) {
+    if ((code & 0x7Fu) == 0x7Fu) return NAN; /* S.1111.111 */
+    double mag = e4m3_magnitude(code & 0x7Fu);
+    return (code & 0x80u) ? -mag : mag;
+}
+
+/* Round an fp32 value to E4M3: nearest, ties to even, saturating at 448.
+ * The 127 non-negative finite codes 0..126 are in increasing order of value,
+ * so the code below |v| is found by bisection and the decision against the
+ * midpoint of the two neighbouring values is exact in double (both the fp32
+ * input and the midpoint are exactly representable). */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80u : 0x00u;
+    double a = fabs((double)v);
+    unsigned c;
+    if (a >= 448.0) {
+        c = 126; /* 0x7E = 448, the largest finite value: saturate */
+    } else {
+        unsigned lo = 0, hi = 126; /* invariant: value(lo) <= a < value(hi+1) */
+        while (lo < hi) {
+            unsigned mid = (lo + hi + 1) / 2;
+            if (e4m3_magnitude(mid) <= a) lo = mid;
+            else hi = mid - 1;
+        }
+        c = lo;
+        if (c < 126) {
+            double half = (e4m3_magnitude(c) + e4m3_magnitude(c + 1)) / 2.0;
+            if (a > half || (a == half && (c & 1u))) c += 1; /* tie: even code */
+        }
+    }
+    return (uint8_t)(sign | c);
+}
+
+/* The encoder applied element-wise to an array (for tests over many inputs). */
+void oracle_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_encode(v[i]);
+}
+
+/* Encode one value x of a group whose scale is s (s >= 0). */
+static uint8_t quantize_one(float x, float s) {
+    if (s == 0.0f) return signbit(x) ? 0x80u : 0x00u; /* all-zero group */
+    return oracle_e4m3_encode(x / s);
+}
+
+/* ---- quantizers -------------------------------------------------------------
+ * Return 0 on success, -1 for bad shapes, -2 if a non-finite input was seen
+ * (finite input is a precondition; outputs are then unspecified). */
+
+int oracle_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s) {
+    if (M < 0 || K < 0 || K % GROUP) return -1;
+    int64_t KB = K / GROUP;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            const uint16_t *g = x + m * K + kb * GROUP;
+            float amax = 0.0f;
+            for (int j = 0; j < GROUP; j++) {
+                float v = bf16_to_f32(g[j]);
+                if (!isfinite(v)) bad = 1;
+                float av = fabsf(v);
+                if (av > amax) amax = av;
+            }
+            float scale = amax / 448.0f;
+            s[kb * M + m] = scale;
+            for (int j = 0; j < GROUP; j++) q[m * K + kb * GROUP + j] = quantize_one(bf16_to_f32(g[j]), scale);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s) {
+    if (N < 0 || K < 0 || N % GROUP || K % GROUP) return -1;
+    int64_t NB = N / GROUP, KB = K / GROUP;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : bad)
+    for (int64_t nb = 0; nb < NB; nb++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            float amax = 0.0f;
+            for (int64_t i = 0; i < GROUP; i++) {
+                const uint16_t *row = w + (nb * GROUP + i) * K + kb * GROUP;
+                for (int j = 0; j < GROUP; j++) {
+                    float v = bf16_to_f32(row[j]);
+                    if (!isfinite(v)) bad = 1;
+                    float av = fabsf(v);
+                    if (av > amax) amax = av;
+                }
+            }
+            float scale = amax / 448.0f;
+            s[nb * KB + kb] = scale;
+            for (int64_t i = 0; i < GROUP; i++) {
+                int64_t off = (nb * GROUP + i) * K + kb * GROUP;
+                for (int j = 0; j < GROUP; j++) q[off + j] = quantize_one(bf16_to_f32(w[off + j]), scale);
+            }
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---- block-scaled GEMM ------------------------------------------------------
+ * C[m,n] = sum_k (dec(qa[m,k]) * s_a[k/128][m]) * (dec(qw[n,k]) * s_w[n/128][k/128])
+ * evaluated in double for an explicit list of (m, n) output elements, together
+ * with B[m,n] = sum_k |dec(qa[m,k]) * s_a| * |dec(qw[n,k]) * s_w|. */
+
+static double dot_dequant(const uint8_t *qa_row, const float *sa, int64_t M, int64_t m, const uint8_t *qw_row,
+                          const float *sw_rowblock, int64_t K, double *bound) {
+    double c = 0.0, b = 0.0;
+    for (int64_t k = 0; k < K; k++) {
+        int64_t kb = k / GROUP;
+        double a_deq = oracle_e4m3_decode(qa_row[k]) * (double)sa[kb * M + m];
+        double w_deq = oracle_e4m3_decode(qw_row[k]) * (double)sw_rowblock[kb];
+        c += a_deq * w_deq;
+        b += fabs(a_deq) * fabs(w_deq);
+    }
+    *bound = b;
+    return c;
+}
+
+int oracle_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, int64_t M,
+                            int64_t N, int64_t K, const int64_t *ms, const int64_t *ns, int64_t count, double *C,
+                            double *B) {
+    if (M < 0 || N < 0 || K < 0 || N % GROUP || K % GROUP) return -1;
+    for (int64_t i = 0; i < count; i++)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+    int64_t KB = K / GROUP;
+#pragma omp parallel for schedule(dynamic, 256)
+    for (int64_t i = 0; i < count; i++) {
+        int64_t m = ms[i], n = ns[i];
+        C[i] = dot_dequant(qa + m * K, sa, M, m, qw + n * K, sw + (n / GROUP) * KB, K, &B[i]);
+    }
+    return 0;
+}
+
+/* Grouped (MoE) variant: rows [off[e], off[e+1]) of A belong to expert e and
+ * use W_e = qw[e] ([N][K]) with scales sw[e] ([N/128][K/128]).  The offsets are
+ * non-decreasing with off[0] = 0 and off[E] = M_total. */
+int oracle_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
+                                    const int32_t *off, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                    const int64_t *ms, const int64_t *ns, int64_t count, double *C, double *B) {
+    if (E < 1 || M_total < 0 || N < 0 || K < 0 || N % GROUP || K % GROUP) return -1;
+    if (off[0] != 0 || off[E] != M_total) return -1;
+    for (int64_t e = 0; e < E; e++)
+        if (off[e + 1] < off[e]) return -1;
+    for (int64_t i = 0; i < count; i++)
+        if (ms[i] < 0 || ms[i] >= M_total || ns[i] < 0 || ns[i] >= N) return -1;
+    int64_t KB = K / GROUP, NB = N / GROUP;
+#pragma omp parallel for schedule(dynamic, 256)
+    for (int64_t i = 0; i < count; i++) {
+        int64_t m = ms[i], n = ns[i];
+        int64_t e = 0;
+        while (!(off[e] <= m && m < off[e + 1])) e++; /* the segment holding row m */
+        const uint8_t *w_e = qw + e * N * K;
+        const float *s_e = sw + e * NB * KB;
+        C[i] = dot_dequant(qa + m * K, sa, M_total, m, w_e + n * K, s_e + (n / GROUP) * KB, K, &B[i]);
+    }
+    return 0;
+}

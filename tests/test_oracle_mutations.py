@@ -1,0 +1,77 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU; the real oracle is not
+touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm against it.  At least one
+pin must fail for every planted mistake.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_e4m3 as te
+import test_oracle_gemm as tg
+import test_oracle_quant as tq
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "fp8q_oracle.c")).read()
+
+MUTATIONS = {
+    "scale_divisor_447": ("amax / 448.0f", "amax / 447.0f"),
+    "ties_away_from_zero": ("(a == half && (c & 1u))", "(a == half)"),
+    "ties_down": ("(a == half && (c & 1u))", "(a == half && 0)"),
+    "midpoint_inclusive": ("if (a > half ||", "if (a >= half ||"),
+    "sign_dropped": ("return (uint8_t)(sign | c);", "return (uint8_t)c;"),
+    "subnormal_exponent": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "normal_bias_8": ("(int)e - 7)", "(int)e - 8)"),
+    "bf16_widen_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    "act_scale_layout_row_major": ("s[kb * M + m] = scale;", "s[m * KB + kb] = scale;"),
+    "gemm_act_scale_wrong_index": ("(double)sa[kb * M + m]", "(double)sa[m]"),
+    "gemm_weight_scale_dropped": ("* (double)sw_rowblock[kb];", ";"),
+    "gemm_weight_transposed": ("qw + n * K, sw + (n / GROUP) * KB", "qw + n, sw + (n / GROUP) * KB"),
+    "gemm_bound_signed": ("b += fabs(a_deq) * fabs(w_deq);", "b += a_deq * w_deq;"),
+    "weight_amax_one_row": ("const uint16_t *row = w + (nb * GROUP + i) * K + kb * GROUP;",
+                            "const uint16_t *row = w + (nb * GROUP) * K + kb * GROUP;"),
+    "weight_scale_layout": ("s[nb * KB + kb] = scale;", "s[kb * NB + nb] = scale;"),
+    "grouped_expert_off_by_one": ("const uint8_t *w_e = qw + e * N * K;",
+                                  "const uint8_t *w_e = qw + (e > 0 ? e - 1 : 0) * N * K;"),
+    "zero_group_sign_lost": ("return signbit(x) ? 0x80u : 0x00u; /* all-zero group */", "return 0x00u;"),
+}
+
+
+def pins():
+    out = [
+        (te.test_decode_closed_form_points, {}),
+        (te.test_decode_matches_torch_and_is_monotone, {}),
+        (te.test_roundtrip_all_finite_codes, {}),
+        (te.test_encoder_vs_brute_force_all_bf16_quotients, {"amax": 3.5}),
+        (te.test_encoder_signed_zero_and_underflow, {}),
+        (tq.test_amax_element_encodes_to_448, {}),
+        (tq.test_negation_flips_sign_bits_only, {}),
+        (tq.test_dequant_error_bound, {}),
+        (tq.test_weight_blocks_use_their_own_scale, {}),
+        (tg.test_hand_worked_gemm, {}),
+        (tg.test_lossless_case_equals_float64_matmul, {"M": 37, "N": 256, "K": 384}),
+        (tg.test_exact_rational_brute_force, {"M": 2, "K": 256}),
+        (tg.test_grouped_lossless_and_padding, {}),
+    ]
+    for case in tq.load_golden()["act_groups"]:
+        out.append((tq.test_hand_worked_activation_groups, {"case": case}))
+    for case in tq.load_golden()["weight_blocks"]:
+        out.append((tq.test_hand_worked_weight_block, {"case": case}))
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    assert SRC.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = tmp_path / f"mut_{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / f"mut_{name}.so")))
+    caught = []
+    for fn, kw in pins():
+        try:
+            fn(lib, **kw)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
