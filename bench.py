@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained FP8 Linear hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident in HBM:
+  1x128 activation quantization  ->  128x128 weight quantization  ->  block-scaled FP8 GEMM (bf16 out).
+(The decode workload starts from pre-quantized weights, so its step has no weight quantization; the MoE
+workload runs the grouped GEMM over expert segments.)
+
+Prints ONE JSON line.  `value` is the step's GEMM work divided by the whole step time (TFLOP/s), so the
+quantizers' time counts against it.  Per-kernel times come from HIP events recorded on the stream the
+kernels are launched on, around every launch of the timed steps.  `roofline` describes the dominant
+kernel (the GEMM) against MI355X's published peaks; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak) + 1x128 quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+DESCRIPTIONS = {
+    "up": "dense FFN up-projection: A bf16 [4096,7168] ~N(0,1) with 72 (1%) outlier channels x20, W bf16 "
+          "[18432,7168] ~N(0,0.02); 1x128 act quant + 128x128 weight quant + block-scaled FP8 GEMM -> bf16 "
+          "[4096,18432]",
+    "down": "dense FFN down-projection: A = bf16(SiLU(x)*y) [4096,18432], W bf16 [7168,18432] ~N(0,0.02); "
+            "1x128 act quant + 128x128 weight quant + block-scaled FP8 GEMM -> bf16 [4096,7168]",
+    "moe": "MoE layer: 8192 tokens x 7168, top-8 of 64 experts (segments padded to 128 rows), expert W bf16 "
+           "[64][2048,7168]; 1x128 act quant of the padded rows + 128x128 weight quant + grouped block-scaled "
+           "FP8 GEMM -> bf16",
+    "decode": "decode-shaped small M: A bf16 [64,7168], W pre-quantized E4M3 [18432,7168] with 128x128 fp32 "
+              "scales; 1x128 act quant + block-scaled FP8 GEMM -> bf16 [64,18432]",
+    "tiny": "tiny: A bf16 [128,512] with 4 outlier channels x50, W bf16 [256,512]; full path -> bf16 [128,256]",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def act_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def w_bytes(N, K):
+    return 2 * N * K + N * K + 4 * (N // 128) * (K // 128)
+
+
+def gemm_bytes(M, N, K, out_bytes=2):
+    return M * K + N * K + 4 * M * (K // 128) + 4 * (N // 128) * (K // 128) + out_bytes * M * N
+
+
+class Workload:
+    """Device-resident inputs and outputs, plus the list of kernels one step launches."""
+
+    def __init__(self, name):
+        import torch
+
+        import fine_grained_quantization_amd as fq
+        import workloads as wl
+
+        self.name = name
+        dev = "cuda"
+        t0 = time.time()
+        d = wl.WORKLOADS[name]()
+        log(f"[bench] generated {name} inputs in {time.time() - t0:.1f}s")
+        self.host = d
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        M, N, K = d["M"], d["N"], d["K"]
+        self.M, self.N, self.K = M, N, K
+        self.a = bf16(d["a"])
+        self.qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        self.sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+        kernels = [("quant_act_1x128", lambda: fq.fp8q_quant_act_1x128(self.a, self.qa, self.sa),
+                    {"bytes": act_bytes(M, K)})]
+        if name == "decode":
+            self.qw = torch.from_numpy(d["wq"]).to(dev)
+            self.sw = torch.from_numpy(d["sw"]).to(dev)
+        else:
+            self.w = bf16(d["w"])
+            self.qw = torch.empty(d["w"].shape, dtype=torch.uint8, device=dev)
+            lead = tuple(d["w"].shape[:-2])
+            self.sw = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=dev)
+            wrows = int(np.prod(d["w"].shape[:-1]))
+            kernels.append(("quant_w_128x128", lambda: fq.fp8q_quant_w_128x128(self.w, self.qw, self.sw),
+                            {"bytes": w_bytes(wrows, K)}))
+        self.c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if name == "moe":
+            r = d["routing"]
+            self.off = torch.from_numpy(r.offsets).to(dev)
+            E = d["E"]
+            real_rows = int(r.counts.sum())
+            self.flops = 2.0 * real_rows * N * K       # padding rows are not counted as work
+            gb = M * K + E * N * K + 4 * M * (K // 128) + 4 * E * (N // 128) * (K // 128) + 2 * M * N
+            kernels.append(("grouped_gemm_blockscaled",
+                            lambda: fq.fp8q_grouped_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, self.off,
+                                                                     c=self.c),
+                            {"flops": self.flops, "bytes": gb}))
+        else:
+            self.flops = 2.0 * M * N * K
+            kernels.append(("gemm_blockscaled",
+                            lambda: fq.fp8q_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, c=self.c),
+                            {"flops": self.flops, "bytes": gemm_bytes(M, N, K)}))
+        self.kernels = kernels
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        for i, (_, fn, _) in enumerate(self.kernels):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+
+def cpu_baseline(wk: Workload, target_s: float = 12.0):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload: the 1x128 quantization
+    of `rows` activation rows, the 128x128 quantization of the weight blocks those rows need, and the
+    rows x N output elements of the GEMM.  Reported in the metric's unit (TFLOP/s of GEMM work)."""
+    import oracle
+
+    d = wk.host
+    N, K = wk.N, wk.K
+    lib = oracle.load()
+    if wk.name == "moe":
+        e = 0
+        off = d["routing"].offsets
+        lo, hi = int(off[e]), int(off[e + 1])
+        w_bits, a_src = d["w"][e], d["a"][lo:hi]
+    elif wk.name == "decode":
+        w_bits, a_src = None, d["a"]
+    else:
+        w_bits, a_src = d["w"], d["a"]
+    t0 = time.perf_counter()
+    if w_bits is not None:
+        qw, sw = oracle.quant_w_128x128(w_bits, lib=lib)
+    else:
+        qw, sw = d["wq"], d["sw"]
+    t_w = time.perf_counter() - t0
+    # calibrate the GEMM rate on one row, then size the sample to about `target_s` seconds in total
+    qa, sa = oracle.quant_act_1x128(a_src[:1], lib=lib)
+    t1 = time.perf_counter()
+    oracle.gemm_blockscaled(qa, sa, qw, sw, rows=[0], lib=lib)
+    per_row = time.perf_counter() - t1
+    rows = int(max(1, min(a_src.shape[0], (target_s - t_w) / max(per_row, 1e-6))))
+    t2 = time.perf_counter()
+    qa, sa = oracle.quant_act_1x128(a_src[:rows], lib=lib)
+    oracle.gemm_blockscaled(qa, sa, qw, sw, rows=np.arange(rows), lib=lib)
+    t_rows = time.perf_counter() - t2
+    total = t_w + t_rows
+    flops = 2.0 * rows * N * K
+    what = "expert 0's weights" if wk.name == "moe" else ("pre-quantized weights" if wk.name == "decode" else
+                                                         "all weights")
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"{rows} token rows x all {N} outputs (K={K}): their 1x128 quantization, 128x128 "
+                      f"quantization of {what}, and the double-precision GEMM of those rows; {total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="up", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built and measured for a "
+              f"single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fine_grained_quantization_amd as fq
+
+    fq.load_library()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    wk = Workload(args.workload)
+    for _ in range(args.warmup):
+        wk.step()
+    torch.cuda.synchronize()
+
+    nk = len(wk.kernels)
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(nk)]
+              for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        wk.step(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+
+    kernels = {}
+    for i, (kname, _, work) in enumerate(wk.kernels):
+        us = 1e3 * float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+        info = {"us": round(us, 2)}
+        if "flops" in work:
+            info["TFLOP/s"] = round(work["flops"] / us / 1e6, 1)
+            info["frac_fp8_peak"] = round(work["flops"] / us / 1e6 / PEAK_FP8_TFLOPS, 4)
+        info["GB/s"] = round(work["bytes"] / us / 1e3, 1)
+        info["frac_hbm"] = round(work["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4)
+        kernels[kname] = info
+
+    gname, _, gwork = wk.kernels[-1]
+    g = kernels[gname]
+    if args.workload == "decode":
+        roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"kernel": gname, "bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,
+                   "K": wk.K, "out": "bf16", "parallelism": "single GPU"},
+        "kernels": kernels,
+        "roofline": roof,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wk)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

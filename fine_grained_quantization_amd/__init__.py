@@ -1,0 +1,21 @@
+"""Fine-grained FP8 quantization and block-scaled FP8 GEMM for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libfp8q.so`` (hand-written HIP kernels behind the C ABI of ``include/fp8q.h``);
+this package is its Python binding.  Entry points (same names as the C functions):
+
+  fp8q_quant_act_1x128(x)                      bf16 [M, K] -> (E4M3 [M, K], fp32 scales [K/128, M])
+  fp8q_quant_w_128x128(w)                      bf16 [N, K] -> (E4M3 [N, K], fp32 scales [N/128, K/128])
+  fp8q_gemm_blockscaled(qa, sa, qw, sw)        -> C = A W^T, bf16 or fp32 [M, N]
+  fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets)   MoE experts, one segment of rows each
+"""
+from ._binding import (  # noqa: F401
+    OUT_BF16,
+    OUT_F32,
+    LIB_PATH,
+    fp8q_gemm_blockscaled,
+    fp8q_grouped_gemm_blockscaled,
+    fp8q_quant_act_1x128,
+    fp8q_quant_w_128x128,
+    load_library,
+    status_string,
+)

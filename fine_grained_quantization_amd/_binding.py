@@ -1,0 +1,178 @@
+"""ctypes binding of ``libfp8q.so`` (the C ABI declared in ``include/fp8q.h``).
+
+Argument marshalling only: every step runs in the HIP library.  torch provides device memory and the
+current stream; outputs are allocated with torch when the caller does not pass them.  If the library
+is not built, every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+OUT_BF16 = 0
+OUT_F32 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfp8q.so and declare the C signatures.  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIB_PATH:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"fp8q HIP library not found at {path}; build it with "
+                               "`python -m fine_grained_quantization_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.fp8q_quant_act_1x128.argtypes = [P, I64, I64, P, P, P]
+        lib.fp8q_quant_w_128x128.argtypes = [P, I64, I64, P, P, P]
+        lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
+        lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
+        for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_gemm_blockscaled,
+                  lib.fp8q_grouped_gemm_blockscaled):
+            f.restype = ctypes.c_int
+        lib.fp8q_status_string.argtypes = [I]
+        lib.fp8q_status_string.restype = ctypes.c_char_p
+        lib.fp8q_version.argtypes = []
+        lib.fp8q_version.restype = ctypes.c_int
+        if path == LIB_PATH:
+            _lib = lib
+        return lib
+
+
+def status_string(rc: int) -> str:
+    return load_library().fp8q_status_string(rc).decode()
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise RuntimeError(f"{name}: {status_string(rc)}")
+
+
+def _stream_ptr(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() not in (ndim if isinstance(ndim, tuple) else (ndim,)):
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fp8q_quant_act_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                         stream=None):
+    """1x128 activation quantization.  ``x`` bf16 [M, K] -> ``(q uint8 [M, K], s float32 [K/128, M])``."""
+    _need(x, "x", _BF16, 2)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _need(q, "q", _FP8)
+    _need(s, "s", (torch.float32,))
+    if q.numel() != M * K or s.numel() != (K // 128) * M:
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
+           "fp8q_quant_act_1x128")
+    return q, s
+
+
+def fp8q_quant_w_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                         stream=None):
+    """128x128 weight quantization.  ``w`` bf16 [N, K] (or an expert stack [E, N, K]) ->
+    ``(q uint8, s float32 [N/128, K/128])`` (``[E, N/128, K/128]`` for a stack)."""
+    _need(w, "w", _BF16, (2, 3))
+    lead = tuple(w.shape[:-2])
+    N, K = w.shape[-2:]
+    rows = N * (lead[0] if lead else 1)
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=w.device)
+    _need(q, "q", _FP8)
+    _need(s, "s", (torch.float32,))
+    if q.numel() != w.numel() or s.numel() != (rows // 128) * (K // 128):
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_quant_w_128x128(_ptr(w), rows, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
+           "fp8q_quant_w_128x128")
+    return q, s
+
+
+def _out_code(out_dtype):
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    if out_dtype == torch.float32:
+        return OUT_F32
+    raise ValueError(f"out_dtype must be torch.bfloat16 or torch.float32, got {out_dtype}")
+
+
+def fp8q_gemm_blockscaled(qa, sa, qw, sw, out_dtype=torch.bfloat16, c=None, stream=None):
+    """Block-scaled FP8 GEMM ``C = A W^T``.  ``qa`` [M, K], ``sa`` [K/128, M], ``qw`` [N, K],
+    ``sw`` [N/128, K/128] -> ``c`` [M, N] in ``out_dtype`` (bf16 or fp32)."""
+    _need(qa, "qa", _FP8, 2)
+    _need(qw, "qw", _FP8, 2)
+    _need(sa, "sa", (torch.float32,))
+    _need(sw, "sw", (torch.float32,))
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or sa.numel() != (K // 128) * M or sw.numel() != (N // 128) * (K // 128):
+        raise ValueError("inconsistent GEMM operand shapes")
+    code = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _need(c, "c", (out_dtype,))
+    if c.numel() != M * N:
+        raise ValueError("c has the wrong size")
+    _check(load_library().fp8q_gemm_blockscaled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(c), code, M, N, K,
+                                                _stream_ptr(stream)), "fp8q_gemm_blockscaled")
+    return c
+
+
+def fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets, out_dtype=torch.bfloat16, c=None, stream=None):
+    """Grouped (MoE) block-scaled FP8 GEMM.  ``qa`` [M_total, K], ``sa`` [K/128, M_total], ``qw`` [E, N, K],
+    ``sw`` [E, N/128, K/128], ``offsets`` int32 device [E+1] -> ``c`` [M_total, N]."""
+    _need(qa, "qa", _FP8, 2)
+    _need(qw, "qw", _FP8, 3)
+    _need(sa, "sa", (torch.float32,))
+    _need(sw, "sw", (torch.float32,))
+    _need(offsets, "offsets", (torch.int32,), 1)
+    M, K = qa.shape
+    E, N, K2 = qw.shape
+    if K2 != K or sa.numel() != (K // 128) * M or sw.numel() != E * (N // 128) * (K // 128) or \
+            offsets.numel() != E + 1:
+        raise ValueError("inconsistent grouped GEMM operand shapes")
+    code = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _need(c, "c", (out_dtype,))
+    if c.numel() != M * N:
+        raise ValueError("c has the wrong size")
+    _check(load_library().fp8q_grouped_gemm_blockscaled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(c), code,
+                                                        _ptr(offsets), E, M, N, K, _stream_ptr(stream)),
+           "fp8q_grouped_gemm_blockscaled")
+    return c

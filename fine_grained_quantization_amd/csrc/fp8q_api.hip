@@ -1,0 +1,116 @@
+// C-ABI entry points of the fp8q library (declared in include/fp8q.h): argument and device
+// validation, then one launch on the caller's stream.  No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8q.h"
+#include "fp8q_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per device: 0 = not yet checked, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return FP8Q_ERR_NO_DEVICE;
+    }
+    if (dev >= kMaxDevices) return FP8Q_ERR_UNSUPPORTED_DEVICE;
+    int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return FP8Q_ERR_NO_DEVICE;
+        }
+        kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_kind[dev].store(kind, std::memory_order_relaxed);
+    }
+    return kind == 1 ? FP8Q_OK : FP8Q_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // 1-D grids: workgroup count must fit in 31 bits
+
+int finish(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8q_version(void) { return 100; }
+
+const char *fp8q_status_string(int status) {
+    switch (status) {
+        case FP8Q_OK: return "FP8Q_OK: success";
+        case FP8Q_ERR_NULL: return "FP8Q_ERR_NULL: a required pointer is NULL";
+        case FP8Q_ERR_SHAPE: return "FP8Q_ERR_SHAPE: invalid shape (negative size, K or N not a multiple of 128, or bad grouping)";
+        case FP8Q_ERR_ALIGN: return "FP8Q_ERR_ALIGN: a tensor base address is not 16-byte aligned";
+        case FP8Q_ERR_DTYPE: return "FP8Q_ERR_DTYPE: unknown output dtype";
+        case FP8Q_ERR_NO_DEVICE: return "FP8Q_ERR_NO_DEVICE: no HIP device available";
+        case FP8Q_ERR_UNSUPPORTED_DEVICE: return "FP8Q_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950 (MI355X)";
+        case FP8Q_ERR_HIP: return "FP8Q_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "fp8q: unknown status";
+    }
+}
+
+int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream) {
+    if (M < 0 || K < 0 || K % 128) return FP8Q_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8Q_ERR_ALIGN;
+    if (((M + 15) / 16) * ((K / 128 + 3) / 4) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_quant_act_1x128(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream) {
+    if (N < 0 || K < 0 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!w || !q || !s) return FP8Q_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return FP8Q_ERR_ALIGN;
+    if ((N / 128) * (K / 128) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_quant_w_128x128(w, N, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                          int out_dtype, int64_t M, int64_t N, int64_t K, void *stream) {
+    if (M < 0 || N < 0 || K < 128 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!qa || !sa || !qw || !sw || !c) return FP8Q_ERR_NULL;
+    if (!aligned16(qa) || !aligned16(sa) || !aligned16(qw) || !aligned16(sw) || !aligned16(c)) return FP8Q_ERR_ALIGN;
+    if (fp8q::gemm_blocks(M, N) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_gemm_blockscaled(qa, sa, qw, sw, c, out_dtype == FP8Q_OUT_BF16, M, N, K,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                                  int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
+                                  int64_t K, void *stream) {
+    if (E < 1 || M_total < 0 || M_total % 128 || N < 0 || K < 128 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (M_total > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;  // offsets are int32
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
+    if (M_total == 0 || N == 0) return FP8Q_OK;
+    if (!qa || !sa || !qw || !sw || !c || !off) return FP8Q_ERR_NULL;
+    if (!aligned16(qa) || !aligned16(sa) || !aligned16(qw) || !aligned16(sw) || !aligned16(c)) return FP8Q_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(off) & 3u) != 0) return FP8Q_ERR_ALIGN;
+    if (fp8q::gemm_blocks(M_total, N) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_grouped_gemm_blockscaled(qa, sa, qw, sw, c, out_dtype == FP8Q_OUT_BF16, off, E,
+                                                        M_total, N, K, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 kernels of the fp8q library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is read once).
+__device__ __forceinline__ u32x4 load_stream16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// RN64(1/448).  For every bf16 amax, fl32((double)amax * kInv448) equals the IEEE fp32 quotient
+// amax / 448.0f: the double product is within 2^-52 (relative) of amax/448, while amax/448 stays
+// at least 2^-28 (relative) away from every fp32 rounding midpoint and never sits on one, so both
+// round to the same fp32 value.
+constexpr double kInv448 = 1.0 / 448.0;
+
+// Low / high bf16 halves of a packed dword, widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+__device__ __forceinline__ float absmax2(float m, uint32_t d) {
+    return fmaxf(m, fmaxf(fabsf(bf16_lo(d)), fabsf(bf16_hi(d))));
+}
+
+// Scale of a group from its max-abs: fl32(amax / 448).
+__device__ __forceinline__ float group_scale(float amax) { return (float)((double)amax * kInv448); }
+
+// Reciprocal of the scale in double; 0 for an all-zero group, whose elements are then +-0 and
+// encode to sign-preserving zero codes.
+__device__ __forceinline__ double scale_reciprocal(float s) { return s > 0.0f ? 1.0 / (double)s : 0.0; }
+
+// fl32(x / s) for a bf16 x, computed as fl32((double)x * RN64(1/s)).  The double product carries
+// at most ~2^-52 relative error; a quotient of a bf16 (8-bit significand) by an fp32 (24-bit)
+// is either exactly representable in fp32 or at least 2^-49 (relative) away from every fp32
+// rounding midpoint, so the final rounding to fp32 returns the correctly rounded quotient.
+// (Checked exhaustively on the CPU over every bf16 x and every bf16 amax with |x| <= amax.)
+__device__ __forceinline__ float quotient(float x, double inv_s) { return (float)((double)x * inv_s); }
+
+// Encode 4 fp32 quotients (|v| <= 448 * (1 + 2^-23)) to OCP E4M3 codes packed little-endian in a
+// dword.  v_cvt_pk_fp8_f32 rounds to nearest even and, on gfx950, encodes OCP E4M3 ("FN").
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+// Quantize the 4 bf16 values of two packed dwords to 4 codes (element order preserved).
+__device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, double inv_s) {
+    return encode4(quotient(bf16_lo(d0), inv_s), quotient(bf16_hi(d0), inv_s), quotient(bf16_lo(d1), inv_s),
+                   quotient(bf16_hi(d1), inv_s));
+}
+
+// Cross-lane max within aligned groups of 4 lanes (DPP quad permutations, no LDS traffic).
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
+    return v;
+}
+
+// Max over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// OCP E4M3 x E4M3 -> fp32 matrix multiply-accumulate, 16x16 output, K = 128 (one scale block).
+// Operand lane layout: lane l supplies row (l % 16) and bytes [(l / 16) * 32, +32) of that row's
+// 128 K-elements, for both operands; the result lane l, register r holds row 4 * (l / 16) + r,
+// column l % 16.  Zero scale operands select the unscaled instruction (scale 1).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Pack two fp32 into two bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace fp8q

@@ -1,0 +1,20 @@
+// Host-side launchers of the fp8q gfx950 kernels.  Arguments are validated by the C-ABI layer
+// (fp8q_api.hip) before any of these is called; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, hipStream_t stream);
+hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                                   bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
+                                           void *c, bool out_bf16, const int32_t *off, int64_t E, int64_t M_total,
+                                           int64_t N, int64_t K, hipStream_t stream);
+// Number of workgroups the dense GEMM launches for an M x N output (for grid-size validation).
+int64_t gemm_blocks(int64_t M, int64_t N);
+
+}  // namespace fp8q

@@ -1,0 +1,124 @@
+// Fine-grained FP8 quantization kernels for gfx950: 1x128 activation tiles and 128x128 weight
+// blocks (page "The Definitive Information To Deepseek", the passage referring to Figure 7 (a)).
+//
+// Both kernels are HBM-bound streams: 2 bytes of bf16 read, 1 byte of E4M3 written per element
+// (plus one fp32 scale per group).  Loads are 16-byte, fully coalesced per instruction; the
+// group's max-abs is reduced in registers (DPP / shuffles), never through HBM; every element is
+// read exactly once.
+#include "fp8q_device.h"
+#include "fp8q_kernels.h"
+
+namespace fp8q {
+
+// ---------------------------------------------------------------------------------------------
+// 1x128 activations.  A wave quantizes one K-block (128 channels) of 16 consecutive tokens; each
+// group of 128 elements (256 bytes) is shared by 4 lanes.  In load j (0..3) lane quarter t reads
+// bytes [64 j + 16 t, +16) of its group, so the 4 lanes of a group read 64 contiguous bytes per
+// instruction.  A workgroup's 4 waves take 4 consecutive K-blocks of the same 16 tokens.  The 16
+// scales a wave produces are consecutive in the K-block-major s_a layout (64-byte store).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                              uint8_t *__restrict__ q, float *__restrict__ s) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t KB = K >> 7;
+    const int64_t KQ = (KB + 3) >> 2;  // K-block quads
+    const int64_t kb = ((int64_t)blockIdx.x % KQ) * 4 + wave;
+    if (kb >= KB) return;  // wave-uniform; no barriers in this kernel
+    const int64_t m = ((int64_t)blockIdx.x / KQ) * 16 + (lane >> 2);
+    const int t = lane & 3;
+    const bool valid = m < M;
+    const int64_t mr = valid ? m : M - 1;  // tail lanes re-read the last row and store nothing
+
+    const uint16_t *src = x + mr * K + kb * 128 + t * 8;
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = load_stream16(src + j * 32);
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        amax = absmax2(amax, v[j].x);
+        amax = absmax2(amax, v[j].y);
+        amax = absmax2(amax, v[j].z);
+        amax = absmax2(amax, v[j].w);
+    }
+    amax = quad_max(amax);
+    const float sc = group_scale(amax);
+    const double inv = scale_reciprocal(sc);
+
+    if (valid) {
+        uint8_t *dst = q + m * K + kb * 128 + t * 8;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            uint2 o;
+            o.x = quant4(v[j].x, v[j].y, inv);
+            o.y = quant4(v[j].z, v[j].w, inv);
+            *reinterpret_cast<uint2 *>(dst + j * 32) = o;
+        }
+        if (t == 0) s[kb * M + m] = sc;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 128x128 weights.  One workgroup (256 threads) per block.  In load i (0..7) thread t reads the
+// 16-byte chunk (t % 16) of block row (t / 16 + 16 i): 16 threads cover a 256-byte row, one
+// instruction covers 16 rows.  The block max is a wave reduction plus a 4-entry LDS exchange.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w, int64_t K,
+                                                              uint8_t *__restrict__ q, float *__restrict__ s) {
+    __shared__ float wave_amax[4];
+    const int tid = threadIdx.x;
+    const int64_t KB = K >> 7;
+    const int64_t kb = (int64_t)blockIdx.x % KB;
+    const int64_t nb = (int64_t)blockIdx.x / KB;
+    const int chunk = tid & 15;
+    const int r0 = tid >> 4;
+    const uint16_t *base = w + (nb * 128) * K + kb * 128 + chunk * 8;
+
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = load_stream16(base + (int64_t)(r0 + 16 * i) * K);
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        amax = absmax2(amax, v[i].x);
+        amax = absmax2(amax, v[i].y);
+        amax = absmax2(amax, v[i].z);
+        amax = absmax2(amax, v[i].w);
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) wave_amax[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
+    const float sc = group_scale(amax);
+    const double inv = scale_reciprocal(sc);
+
+    uint8_t *dst = q + (nb * 128) * K + kb * 128 + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        uint2 o;
+        o.x = quant4(v[i].x, v[i].y, inv);
+        o.y = quant4(v[i].z, v[i].w, inv);
+        *reinterpret_cast<uint2 *>(dst + (int64_t)(r0 + 16 * i) * K) = o;
+    }
+    if (tid == 0) s[nb * KB + kb] = sc;
+}
+
+hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
+                                  hipStream_t stream) {
+    const int64_t KQ = (K / 128 + 3) / 4;
+    const int64_t blocks = ((M + 15) / 16) * KQ;  // 1-D grid: K-block quad fastest
+    quant_act_1x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                                  hipStream_t stream) {
+    const int64_t blocks = (N / 128) * (K / 128);  // 1-D grid: K-block fastest
+    quant_w_128x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -1,0 +1,121 @@
+/*
+ * fp8q.h -- C ABI of the fine-grained FP8 quantization / block-scaled FP8 GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "The Definitive Information To Deepseek", DeepSeek-V3's FP8
+ * mixed-precision framework):
+ *   - activations are scaled and quantized online per 1x128 tile (one token,
+ *     128 consecutive channels), weights per 128x128 block (the passage that
+ *     refers to Figure 7 (a));
+ *   - the scale of a group is derived from the group and the group is then
+ *     encoded in FP8 (the passage on caching the Linear input in FP8); this
+ *     library reads it as scale = fl32(amax / 448) with OCP E4M3 codes, round
+ *     to nearest even, saturating at +-448;
+ *   - the GEMMs take FP8 operands and produce BF16 or FP32 (the passage on the
+ *     GEMM inputs and outputs), and partial sums are promoted into an FP32
+ *     accumulator with the per-block scales (the passage on promotion running
+ *     beside the MMA on H800); the promotion interval here is every 128
+ *     elements of K.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *     and contiguous, with base addresses aligned to 16 bytes.  The library
+ *     never allocates, frees or synchronizes.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  FP8 tensors are
+ *     uint8_t OCP E4M3 codes (0x7F / 0xFF are NaN and never produced).
+ *   - Scales are fp32.  Activation scales s_a have layout [K/128][M]
+ *     (K-block-major: element (kb, m) at s_a[kb * M + m]).  Weight scales s_w
+ *     have layout [N/128][K/128] (element (nb, kb) at s_w[nb * (K/128) + kb]).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; results are visible after the caller
+ *     synchronizes that stream.  The same inputs always give bit-identical
+ *     outputs.
+ *   - Every call validates its arguments and the current device before any
+ *     launch and returns FP8Q_OK or a negative fp8q_status.  On error nothing
+ *     is launched and no output is touched.  A launch failure reported by the
+ *     runtime returns FP8Q_ERR_HIP.  Faults during execution (for example a
+ *     host pointer passed as a device pointer) surface at the caller's
+ *     synchronization, as for any HIP kernel.
+ *   - Finite inputs are a precondition.  Shapes are int64_t.  M may be any
+ *     value >= 0 (M == 0 launches nothing); K and N must be multiples of 128.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_NULL = -1,               /* a required pointer is NULL */
+    FP8Q_ERR_SHAPE = -2,              /* negative size, or K / N not a multiple of 128, or bad group layout */
+    FP8Q_ERR_ALIGN = -3,              /* a tensor base address is not 16-byte aligned */
+    FP8Q_ERR_DTYPE = -4,              /* unknown output dtype */
+    FP8Q_ERR_NO_DEVICE = -5,          /* no HIP device is available */
+    FP8Q_ERR_UNSUPPORTED_DEVICE = -6, /* the current device is not gfx950 */
+    FP8Q_ERR_HIP = -7                 /* the HIP runtime reported an error at launch */
+} fp8q_status;
+
+typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 } fp8q_out_dtype;
+
+/* 1x128 activation quantization (the Figure 7 (a) passage: per token per 128
+ * channels).
+ *   x  : bf16 [M, K]            (input)
+ *   q  : E4M3 [M, K]            (output)
+ *   s  : fp32 [K/128][M]        (output; s[kb*M + m] = fl32(max_k |x[m, kb*128+k]| / 448))
+ * q[m,k] = E4M3_RNE_saturating(fl32(x[m,k] / s)), or a signed zero when s == 0.
+ * Requires M >= 0, K >= 0, K % 128 == 0. */
+int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
+
+/* 128x128 weight quantization (the Figure 7 (a) passage: per 128 input
+ * channels per 128 output channels).
+ *   w  : bf16 [N, K]            (input; an expert stack [E][N', K] is passed as N = E * N')
+ *   q  : E4M3 [N, K]            (output)
+ *   s  : fp32 [N/128][K/128]    (output; the block's fl32(amax / 448))
+ * Requires N % 128 == 0, K % 128 == 0. */
+int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
+
+/* Block-scaled FP8 GEMM, the Linear y = x W^T (the passages on FP8 GEMM inputs
+ * with BF16/FP32 outputs and on FP32 promotion):
+ *   C[m,n] = sum_kb  s_a[kb][m] * s_w[n/128][kb] * (sum_{k in kb} qa[m,k] * qw[n,k])
+ * with each 128-element partial sum promoted into an fp32 accumulator.
+ *   qa : E4M3 [M, K],  sa : fp32 [K/128][M]
+ *   qw : E4M3 [N, K],  sw : fp32 [N/128][K/128]
+ *   c  : [M, N] bf16 (out_dtype FP8Q_OUT_BF16, round to nearest even) or fp32 (FP8Q_OUT_F32)
+ * Requires M >= 0, N % 128 == 0, K % 128 == 0, K >= 128. */
+int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                          int out_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Grouped block-scaled FP8 GEMM for MoE experts (one Linear per expert; the
+ * token-to-expert layout is the caller's):
+ *   rows [off[e], off[e+1]) of A are multiplied by expert e's weight.
+ *   qa  : E4M3 [M_total, K],      sa : fp32 [K/128][M_total]
+ *   qw  : E4M3 [E][N][K],         sw : fp32 [E][N/128][K/128]
+ *   off : DEVICE int32 [E+1], non-decreasing, off[0] = 0, off[E] = M_total,
+ *         every off[e] a multiple of 128 (segments padded to 128 rows; empty
+ *         experts allowed).  Padding rows should carry codes 0 and scale 0 and
+ *         then produce exact zeros.
+ *   c   : [M_total, N] bf16 or fp32.
+ * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, K >= 128.
+ * The offsets live on the device and are not checked on the host; rows that no
+ * segment covers (only possible when the offsets break the rules above) are
+ * written as zeros, and every memory access stays inside the buffers described
+ * by M_total, E, N and K. */
+int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                                  int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
+                                  int64_t K, void *stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char *fp8q_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fp8q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -53,6 +53,8 @@ def load(path: str | None = None):
         lib = ctypes.CDLL(p)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -70,6 +72,11 @@ def load(path: str | None = None):
         if path is None:
             _lib = lib
         return lib
+
+
+def num_threads(lib=None) -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int((lib or load()).oracle_num_threads())
 
 
 def _ptr(a: np.ndarray):

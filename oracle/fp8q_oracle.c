@@ -51,12 +51,24 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
 #error "the oracle requires float expressions to be evaluated in float"
 #endif
 
 #define GROUP 128
+
+/* Number of threads the parallel loops below use (reported beside oracle timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---- bf16 ---------------------------------------------------------------- */
 

@@ -1,0 +1,84 @@
+"""The C-ABI library loads, exports every entry point that include/fp8q.h declares, and rejects bad
+arguments before touching a device.  No kernel is launched here (CPU-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_quantization_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fq.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return fq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(fp8q_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("fp8q_quant_act_1x128", "fp8q_quant_w_128x128", "fp8q_gemm_blockscaled",
+              "fp8q_grouped_gemm_blockscaled", "fp8q_status_string", "fp8q_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in fp8q.h but not exported"
+
+
+def test_library_contains_gfx950_code():
+    blob = open(fq.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_status_strings(lib):
+    assert lib.fp8q_version() >= 100
+    for code in range(0, -8, -1):
+        assert lib.fp8q_status_string(code).decode().startswith("FP8Q_")
+    assert b"unknown" in lib.fp8q_status_string(42)
+
+
+A = ctypes.c_void_p(4096)      # aligned dummy addresses: never dereferenced, every call below fails validation
+B = ctypes.c_void_p(8192)
+MIS = ctypes.c_void_p(4098)
+
+
+def test_argument_validation_without_device(lib):
+    # shape errors come first
+    assert lib.fp8q_quant_act_1x128(A, 4, 100, B, B, None) == -2
+    assert lib.fp8q_quant_act_1x128(A, -1, 128, B, B, None) == -2
+    assert lib.fp8q_quant_w_128x128(A, 100, 128, B, B, None) == -2
+    assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 0, 4, 100, 128, None) == -2
+    assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 0, 4, 128, 64, None) == -2
+    assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, A, 0, 128, 128, 128, None) == -2
+    assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, A, 2, 100, 128, 128, None) == -2
+    # dtype
+    assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 7, 4, 128, 128, None) == -4
+    # empty problems succeed without work
+    assert lib.fp8q_quant_act_1x128(None, 0, 128, None, None, None) == 0
+    assert lib.fp8q_gemm_blockscaled(None, None, None, None, None, 0, 0, 128, 128, None) == 0
+    # null and alignment
+    assert lib.fp8q_quant_act_1x128(None, 4, 128, B, B, None) == -1
+    assert lib.fp8q_quant_w_128x128(A, 128, 128, None, B, None) == -1
+    assert lib.fp8q_gemm_blockscaled(A, A, A, None, B, 1, 4, 128, 128, None) == -1
+    assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, None, 2, 128, 128, 128, None) == -1
+    assert lib.fp8q_quant_act_1x128(MIS, 4, 128, B, B, None) == -3
+    assert lib.fp8q_gemm_blockscaled(A, A, A, A, MIS, 0, 4, 128, 128, None) == -3
+
+
+def test_valid_call_without_gpu_reports_no_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.fp8q_quant_act_1x128(A, 4, 128, B, B, None) in (-5, -6)
