@@ -37,6 +37,7 @@ int check_device() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // 1-D grids: workgroup count must fit in 31 bits
+constexpr int64_t kMaxK = int64_t(1) << 23;  // GEMM tiles address 256 rows of K bytes with 32-bit offsets
 
 int finish(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
@@ -84,7 +85,7 @@ int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, fl
 
 int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                           int out_dtype, int64_t M, int64_t N, int64_t K, void *stream) {
-    if (M < 0 || N < 0 || K < 128 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (M < 0 || N < 0 || K < 128 || K > kMaxK || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
     if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!qa || !sa || !qw || !sw || !c) return FP8Q_ERR_NULL;
@@ -99,7 +100,8 @@ int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw,
 int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                                   int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
                                   int64_t K, void *stream) {
-    if (E < 1 || M_total < 0 || M_total % 128 || N < 0 || K < 128 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (E < 1 || M_total < 0 || M_total % 128 || N < 0 || K < 128 || K > kMaxK || N % 128 || K % 128)
+        return FP8Q_ERR_SHAPE;
     if (M_total > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;  // offsets are int32
     if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
     if (M_total == 0 || N == 0) return FP8Q_OK;

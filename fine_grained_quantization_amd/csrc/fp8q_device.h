@@ -4,8 +4,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+typedef int fp8q_i32x4 __attribute__((ext_vector_type(4)));
+
+// LLVM's raw buffer load into LDS (buffer_load_dwordx4 ... lds): per-lane byte offset `voffset`, scalar
+// byte offset `soffset`; the `size` bytes of lane l land at the wave's LDS address + size * l.  Reads at
+// or past the resource's byte count return zeros.
+__device__ void fp8q_raw_buffer_load_lds(fp8q_i32x4 rsrc, __attribute__((address_space(3))) void *lds, int size,
+                                         int voffset, int soffset, int offset,
+                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// LLVM's raw buffer loads into registers (16 bytes / 4 bytes per lane); out-of-range reads return 0.
+__device__ fp8q_i32x4 fp8q_raw_buffer_load_b128(fp8q_i32x4 rsrc, int voffset, int soffset,
+                                                int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ float fp8q_raw_buffer_load_f32(fp8q_i32x4 rsrc, int voffset, int soffset,
+                                          int aux) __asm("llvm.amdgcn.raw.buffer.load.f32");
+
 namespace fp8q {
 
+typedef fp8q_i32x4 i32x4;
+
+// A byte offset past every buffer this library builds (they are < 2^31 bytes): loads there return 0
+// without touching memory.
+constexpr int kOutOfRange = 0x7FFFFFF0;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -62,6 +82,14 @@ __device__ __forceinline__ float quad_max(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
     return v;
+}
+
+// Workgroup barrier that only waits for this wave's LDS traffic (not for global loads in flight), so
+// register prefetches of global data survive it.  Enough when the data shared through the barrier was
+// written to LDS with ds_write: s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
 }
 
 // Max over the 64 lanes of a wavefront.

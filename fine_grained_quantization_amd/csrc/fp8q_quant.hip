@@ -20,7 +20,7 @@ namespace fp8q {
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
     const int64_t KB = K >> 7;
     const int64_t KQ = (KB + 3) >> 2;  // K-block quads
     const int64_t kb = ((int64_t)blockIdx.x % KQ) * 4 + wave;

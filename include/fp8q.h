@@ -85,7 +85,7 @@ int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, fl
  *   qa : E4M3 [M, K],  sa : fp32 [K/128][M]
  *   qw : E4M3 [N, K],  sw : fp32 [N/128][K/128]
  *   c  : [M, N] bf16 (out_dtype FP8Q_OUT_BF16, round to nearest even) or fp32 (FP8Q_OUT_F32)
- * Requires M >= 0, N % 128 == 0, K % 128 == 0, K >= 128. */
+ * Requires M >= 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23. */
 int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                           int out_dtype, int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -99,7 +99,7 @@ int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw,
  *         experts allowed).  Padding rows should carry codes 0 and scale 0 and
  *         then produce exact zeros.
  *   c   : [M_total, N] bf16 or fp32.
- * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, K >= 128.
+ * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23.
  * The offsets live on the device and are not checked on the host; rows that no
  * segment covers (only possible when the offsets break the rules above) are
  * written as zeros, and every memory access stays inside the buffers described

@@ -61,6 +61,7 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_quant_w_128x128(A, 100, 128, B, B, None) == -2
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 0, 4, 100, 128, None) == -2
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 0, 4, 128, 64, None) == -2
+    assert lib.fp8q_gemm_blockscaled(A, A, A, A, B, 0, 4, 128, (1 << 23) + 128, None) == -2
     assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, A, 0, 128, 128, 128, None) == -2
     assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, A, 2, 100, 128, 128, None) == -2
     # dtype

@@ -49,7 +49,7 @@ def test_tiny_workload_all_elements(out):
 
 
 SHAPES = [(1, 128, 128), (7, 256, 384), (129, 384, 512), (300, 640, 1024), (257, 256, 2048), (64, 1024, 896),
-          (1000, 128, 256)]
+          (1000, 128, 256), (33, 512, 1152), (64, 128, 2176), (65, 384, 640), (128, 256, 1280), (511, 896, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
