@@ -77,19 +77,21 @@ __device__ __forceinline__ uint32_t quant4(uint32_t d0, uint32_t d1, double inv_
                    quotient(bf16_hi(d1), inv_s));
 }
 
-// Cross-lane max within aligned groups of 4 lanes (DPP quad permutations, no LDS traffic).
-__device__ __forceinline__ float quad_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));  // lane ^ 1
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));  // lane ^ 2
-    return v;
-}
-
 // Workgroup barrier that only waits for this wave's LDS traffic (not for global loads in flight), so
 // register prefetches of global data survive it.  Enough when the data shared through the barrier was
 // written to LDS with ds_write: s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima).
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
+}
+
+// Max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 within the row); every lane gets it.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+    return v;
 }
 
 // Max over the 64 lanes of a wavefront.

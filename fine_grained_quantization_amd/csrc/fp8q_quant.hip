@@ -11,11 +11,12 @@
 namespace fp8q {
 
 // ---------------------------------------------------------------------------------------------
-// 1x128 activations.  A wave quantizes one K-block (128 channels) of 16 consecutive tokens; each
-// group of 128 elements (256 bytes) is shared by 4 lanes.  In load j (0..3) lane quarter t reads
-// bytes [64 j + 16 t, +16) of its group, so the 4 lanes of a group read 64 contiguous bytes per
-// instruction.  A workgroup's 4 waves take 4 consecutive K-blocks of the same 16 tokens.  The 16
-// scales a wave produces are consecutive in the K-block-major s_a layout (64-byte store).
+// 1x128 activations.  A 128-element group (256 bytes of bf16) is spread over the 16 lanes of a DPP row,
+// 8 elements per lane, so its max-abs is 4 row rotations.  Lane l of a wave works on K-block
+// 4 kq + l / 16 (kq = the workgroup's K-block quad) of 4 consecutive tokens, one token per load: each load
+// instruction then reads 4 consecutive K-blocks of one token (1 KB contiguous) and each store writes their
+// 512 code bytes contiguously.  A workgroup (4 waves) covers 16 tokens x 4 K-blocks; its scales are 16
+// consecutive tokens of the K-block-major s_a layout for each of the 4 K-blocks.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
@@ -23,40 +24,38 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
     const int64_t KB = K >> 7;
     const int64_t KQ = (KB + 3) >> 2;  // K-block quads
-    const int64_t kb = ((int64_t)blockIdx.x % KQ) * 4 + wave;
-    if (kb >= KB) return;  // wave-uniform; no barriers in this kernel
-    const int64_t m = ((int64_t)blockIdx.x / KQ) * 16 + (lane >> 2);
-    const int t = lane & 3;
-    const bool valid = m < M;
-    const int64_t mr = valid ? m : M - 1;  // tail lanes re-read the last row and store nothing
+    const int64_t kq = (int64_t)blockIdx.x % KQ;
+    const int64_t row0 = ((int64_t)blockIdx.x / KQ) * 16 + wave * 4;
+    const int64_t kb = kq * 4 + (lane >> 4);
+    const int i = lane & 15;
+    const bool kb_ok = kb < KB;
+    const int64_t kbr = kb_ok ? kb : KB - 1;  // lanes past the last K-block re-read it and store nothing
 
-    const uint16_t *src = x + mr * K + kb * 128 + t * 8;
     u32x4 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = load_stream16(src + j * 32);
-
-    float amax = 0.0f;
+    for (int j = 0; j < 4; j++) {
+        const int64_t m = row0 + j;
+        const int64_t mr = m < M ? m : M - 1;  // tokens past M re-read the last one and store nothing
+        v[j] = load_stream16(x + mr * K + kbr * 128 + i * 8);
+    }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+        float amax = 0.0f;
         amax = absmax2(amax, v[j].x);
         amax = absmax2(amax, v[j].y);
         amax = absmax2(amax, v[j].z);
         amax = absmax2(amax, v[j].w);
-    }
-    amax = quad_max(amax);
-    const float sc = group_scale(amax);
-    const double inv = scale_reciprocal(sc);
-
-    if (valid) {
-        uint8_t *dst = q + m * K + kb * 128 + t * 8;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
+        amax = row16_max(amax);
+        const float sc = group_scale(amax);
+        const double inv = scale_reciprocal(sc);
+        const int64_t m = row0 + j;
+        if (m < M && kb_ok) {
             uint2 o;
             o.x = quant4(v[j].x, v[j].y, inv);
             o.y = quant4(v[j].z, v[j].w, inv);
-            *reinterpret_cast<uint2 *>(dst + j * 32) = o;
+            *reinterpret_cast<uint2 *>(q + m * K + kb * 128 + i * 8) = o;
+            if (i == 0) s[kb * M + m] = sc;
         }
-        if (t == 0) s[kb * M + m] = sc;
     }
 }
 
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
                                   hipStream_t stream) {
     const int64_t KQ = (K / 128 + 3) / 4;
-    const int64_t blocks = ((M + 15) / 16) * KQ;  // 1-D grid: K-block quad fastest
+    const int64_t blocks = ((M + 15) / 16) * KQ;  // 1-D grid: K-block quad fastest, 16 tokens per workgroup
     quant_act_1x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
     return hipGetLastError();
 }
