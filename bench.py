@@ -188,6 +188,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="up", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-copy-mb", type=int, default=0,
+                    help="before warmup, run one plain elementwise copy (torch.neg) of this many MiB; its "
+                         "FETCH_SIZE / WRITE_SIZE under rocprofv3 calibrate the traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built and measured for a "
@@ -201,6 +204,12 @@ def main():
     fq.load_library()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
     wk = Workload(args.workload)
+    if args.pmc_copy_mb:
+        src = torch.ones(args.pmc_copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         wk.step()
     torch.cuda.synchronize()

@@ -218,16 +218,17 @@ __global__ __launch_bounds__(256, 2) void gemm_blockscaled_kernel(const uint8_t 
 }
 
 // =============================================================================================
-// Large-M kernel: 256 x 256 workgroup tile, 8 waves (4 along M x 2 along N, 64 x 128 per wave, so
-// 2 waves share each SIMD and one wave's promotion VALU work overlaps the other's MFMAs).  Global
-// tiles go straight to LDS with buffer loads (no staging registers, K-block offset in a scalar
-// register, rows past the end of the tile's range read as zeros); 2 LDS stages of 64 KB
-// (A 256 x 128 B + W 256 x 128 B).  Each wave's 128 weight rows are exactly one 128-row scale
-// block, so its weight scale is one scalar per K-block.
+// Large-M kernel: 256 x BN workgroup tile (BN = 32 NSUB weight rows, NSUB = 6, 7 or 8), 8 waves: 4 along M
+// x 2 along N, 64 tokens x 16 NSUB weight rows per wave, so 2 waves share each SIMD and one wave's promotion
+// VALU work overlaps the other's MFMAs.  Global tiles go straight to LDS with buffer loads (no staging
+// registers, K-block offset in a scalar register, rows past the end of the tile's range read as zeros);
+// 2 LDS stages of (256 + BN) x 128 B.  The host picks BN so that the number of tiles fills whole rounds of
+// the CUs as far as possible.
 // =============================================================================================
 
-constexpr int kBig = 256;                  // tile rows along M and along N
-constexpr int kStageBytes = 2 * kBig * 128;  // A + W bytes of one K-block
+constexpr int kBig = 256;  // tile rows along M
+
+int cu_count();  // multiprocessor count of the current device (cached)
 
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
@@ -242,12 +243,16 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint64_t bytes) {
     return r;
 }
 
-// Per-lane source offsets of one K-block tile.  Wave w fills tile rows [32 w, 32 w + 32) of A and of W,
-// 8 rows (1 KB) per instruction; lane l of an instruction lands in LDS slot l, i.e. row l / 8, physical
-// chunk l % 8, which must hold logical chunk (l % 8) ^ swzf(row).
+// Per-lane source offsets of one K-block tile.  Rows are copied 8 at a time (1 KB per instruction); lane l of
+// an instruction lands in LDS slot l, i.e. row l / 8 of the 8, physical chunk l % 8, which must hold logical
+// chunk (l % 8) ^ swzf(row).  Wave w copies A rows [32 w, 32 w + 32) and the W row groups g = w, w + 8, ...
+template <int BN>
 struct TileLoader {
-    i32x4 ra, rw;   // resources: this tile's A rows / W rows
-    int voff[4];    // row * K + chunk * 16 for the 4 instructions (same rows in A and W)
+    static constexpr int kWGroups = BN / 8;               // 8-row groups of the weight tile
+    static constexpr int kWPerWave = (kWGroups + 7) / 8;  // groups per wave (the last may be partial)
+    i32x4 ra, rw;             // resources: this tile's A rows / W rows
+    int avoff[4];             // A: row * K + chunk * 16 for the wave's 4 instructions
+    int wvoff[kWPerWave];     // W: same for the wave's weight row groups
     __device__ __forceinline__ void init(const uint8_t *a_rows, uint64_t a_bytes, const uint8_t *w_rows,
                                          uint64_t w_bytes, int64_t K, int wave, int lane) {
         ra = make_rsrc(a_rows, a_bytes);
@@ -255,56 +260,79 @@ struct TileLoader {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int r = wave * 32 + j * 8 + (lane >> 3);
-            voff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
+            avoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kWPerWave; j++) {
+            const int r = (wave + 8 * j) * 8 + (lane >> 3);
+            wvoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
         }
     }
     __device__ __forceinline__ void issue(uint8_t *stage, int koff, int wave) const {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            fp8q_raw_buffer_load_lds(ra, (lds_ptr)(stage + (wave * 32 + j * 8) * 128), 16, voff[j], koff, 0, 0);
-            fp8q_raw_buffer_load_lds(rw, (lds_ptr)(stage + kBig * 128 + (wave * 32 + j * 8) * 128), 16, voff[j], koff,
-                                0, 0);
+        for (int j = 0; j < 4; j++)
+            fp8q_raw_buffer_load_lds(ra, (lds_ptr)(stage + (wave * 32 + j * 8) * 128), 16, avoff[j], koff, 0, 0);
+#pragma unroll
+        for (int j = 0; j < kWPerWave; j++) {
+            const int g = wave + 8 * j;
+            if (g < kWGroups)  // wave-uniform
+                fp8q_raw_buffer_load_lds(rw, (lds_ptr)(stage + kBig * 128 + g * 1024), 16, wvoff[j], koff, 0, 0);
         }
     }
 };
 
-template <bool OUT_BF16, bool GROUPED>
+// Tile coordinates of workgroup t for a dense n_mt x n_nt tile grid.  Workgroups are dispatched to the 8 XCDs
+// round-robin (t % 8), and 256 of them (one per CU) run at a time.  Each run of 256 covers a 16 x 16 square of
+// tiles ("supergroup"), and within it XCD x takes a 4 (M) x 8 (N) block, so the 32 tiles resident on one XCD
+// share 4 activation and 8 weight tile rows in that XCD's L2, and the XCDs together share the square's operands
+// in the Infinity Cache.  Returns false for indices that fall outside the grid.
+__device__ __forceinline__ bool supergroup_tile(int64_t t, int64_t n_mt, int64_t n_nt, int64_t &mt, int64_t &nt) {
+    const int64_t sg = t / 256, j = t % 256;
+    const int64_t x = j % 8, k = j / 8;  // XCD, position within the XCD's 4 x 8 block
+    const int64_t sg_m = (n_mt + 15) / 16;
+    const int64_t sgm = sg % sg_m, sgn = sg / sg_m;
+    mt = sgm * 16 + (x % 4) * 4 + (k % 4);
+    nt = sgn * 16 + (x / 4) * 8 + (k / 4);
+    return mt < n_mt && nt < n_nt;
+}
+
+template <bool OUT_BF16, bool GROUPED, int NSUB>
 __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
                                                              const float *__restrict__ sa,
                                                              const uint8_t *__restrict__ qw,
                                                              const float *__restrict__ sw, void *__restrict__ c,
                                                              int64_t M, int64_t N, int64_t K,
                                                              const int32_t *__restrict__ off, int64_t E,
-                                                             int64_t n_mtiles, int64_t n_tiles) {
+                                                             int64_t n_mtiles, int64_t n_ntiles) {
+    constexpr int BN = 32 * NSUB;
+    constexpr int WN = 16 * NSUB;  // weight rows per wave
+    constexpr int kStageBytes = (kBig + BN) * 128;
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int wm = wave & 3;   // 64-token quarter of the tile
-    const int wn = wave >> 2;  // 128-row half of the weight tile
+    const int wn = wave >> 2;  // weight-row half of the tile
     const int64_t KB = K >> 7;
-
-    // Tiles in launch order, M fastest: the 256 workgroups resident at a time cover all M tiles of a few
-    // N columns, so each K-block slice of A is fetched once per wave of tiles and reused from L2.
-    // (Measured faster than grouping tiles per XCD.)
     const int64_t t = blockIdx.x;
-    if (t >= n_tiles) return;
 
     int64_t m0, mend, n0;
     const uint8_t *W = qw;
     const float *SW = sw;
     if (!GROUPED) {
-        m0 = (t % n_mtiles) * kBig;
-        n0 = (t / n_mtiles) * kBig;
+        int64_t mt, nt;
+        if (!supergroup_tile(t, n_mtiles, n_ntiles, mt, nt)) return;
+        m0 = mt * kBig;
+        n0 = nt * BN;
         mend = M;
     } else {
         // Tiles are enumerated expert by expert: expert e owns ceil(len_e / 256) M tiles of its segment.
         // N is the fastest index here, so the workgroups resident together cover few experts and share
         // both their weights and their activation rows in L2.
-        const int64_t n_ntiles = n_tiles / n_mtiles;  // n_mtiles is an upper bound on the number of M tiles
-        const int64_t mt = t / n_ntiles;
-        n0 = (t % n_ntiles) * kBig;
+        const int64_t mt = t / n_ntiles;  // n_mtiles is an upper bound on the number of M tiles
+        if (mt >= n_mtiles) return;
+        n0 = (t % n_ntiles) * BN;
         int64_t before = 0, e = -1;
         for (int64_t i = 0; i < E; i++) {
             const int64_t lo = off[i], hi = off[i + 1];
@@ -322,24 +350,31 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         SW = sw + e * (N / 128) * KB;
     }
     const int64_t Mlast = mend - 1;
-    TileLoader ld;
+    TileLoader<BN> ld;
     ld.init(qa + m0 * K, (uint64_t)(mend - m0) * (uint64_t)K, W + n0 * K, (uint64_t)(N - n0) * (uint64_t)K, K,
             wave, lane);
 
-    // Scales: this lane's 4 tokens (one per 16-row subtile) and this wave's weight scale block.
+    // Scales: this lane's 4 tokens (one per 16-row subtile).  The wave's weight rows start at nw0; subtiles
+    // ni < nib lie in scale block nbA, the others in nbA + 1 (a 16-row subtile never straddles a 128-row
+    // block).  With NSUB = 8 the waves are aligned to whole blocks and only nbA is used.
     int64_t mrow[4];
 #pragma unroll
     for (int mi = 0; mi < 4; mi++) {
         const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
         mrow[mi] = m < Mlast ? m : Mlast;
     }
-    int64_t nb = (n0 + wn * 128) / 128;
-    nb = nb < N / 128 ? nb : N / 128 - 1;
-    const float *sw_row = SW + nb * KB;
+    const int64_t nw0 = n0 + wn * WN;
+    const int64_t NBmax = N / 128 - 1;
+    int64_t nbA = nw0 / 128;
+    nbA = nbA < NBmax ? nbA : NBmax;
+    const int64_t nbB = nbA + 1 < NBmax ? nbA + 1 : NBmax;
+    const int nib = (int)((128 * (nw0 / 128 + 1) - nw0) / 16);
+    const float *swA_row = SW + nbA * KB;
+    const float *swB_row = SW + nbB * KB;
 
-    v4f acc[8][4];
+    v4f acc[NSUB][4];
 #pragma unroll
-    for (int ni = 0; ni < 8; ni++)
+    for (int ni = 0; ni < NSUB; ni++)
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) acc[ni][mi] = (v4f){0.f, 0.f, 0.f, 0.f};
 
@@ -347,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
     float sa_cur[4], sa_nxt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa[mrow[mi]];
-    float sw_cur = sw_row[0], sw_nxt = 0.f;
+    float swA = swA_row[0], swB = swB_row[0], swA_n = 0.f, swB_n = 0.f;
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
     for (int64_t kb = 0; kb < KB; kb++) {
@@ -363,25 +398,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
             ld.issue(nxt, kb + 1 < KB ? (int)((kb + 1) * 128) : kOutOfRange, wave);
 #pragma unroll
             for (int mi = 0; mi < 4; mi++) sa_nxt[mi] = sa[kn * M + mrow[mi]];
-            sw_nxt = sw_row[kn];
+            swA_n = swA_row[kn];
+            swB_n = swB_row[kn];
         }
-        float cs[4];
+        float csA[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; mi++) cs[mi] = sa_cur[mi] * sw_cur;
+        for (int mi = 0; mi < 4; mi++) csA[mi] = sa_cur[mi] * swA;
+        // The first weight fragment is read before the activation fragments so that the first MFMA waits
+        // for two LDS reads, not five.  The fragment of weight subtile ni+1 is read while the 4 MFMAs of
+        // subtile ni run; their partials are promoted right after issue (the first MFMA has finished by
+        // the time the 4th issues).
+        const uint8_t *tW = cur + kBig * 128;
+        v8i wf = load_frag(tW, wn * WN, lane);
         v8i af[4];
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) af[mi] = load_frag(cur, wm * 64 + mi * 16, lane);
-        const uint8_t *tW = cur + kBig * 128;
-        // The fragment of weight subtile ni+1 is read from LDS while the 4 MFMAs of subtile ni run; their
-        // partials are promoted right after issue (the first MFMA has finished by the time the 4th issues).
-        v8i wf = load_frag(tW, wn * 128, lane);
 #pragma unroll
-        for (int ni = 0; ni < 8; ni++) {
+        for (int ni = 0; ni < NSUB; ni++) {
             v8i wf_next = wf;
-            if (ni < 7) wf_next = load_frag(tW, wn * 128 + (ni + 1) * 16, lane);
+            if (ni < NSUB - 1) wf_next = load_frag(tW, wn * WN + (ni + 1) * 16, lane);
             v4f p[4];
 #pragma unroll
             for (int mi = 0; mi < 4; mi++) p[mi] = mfma_fp8_16x16x128(wf, af[mi], zero);
+            float cs[4];
+            if (NSUB == 8) {
+#pragma unroll
+                for (int mi = 0; mi < 4; mi++) cs[mi] = csA[mi];
+            } else {
+                const float swv = ni < nib ? swA : swB;  // scalar select
+#pragma unroll
+                for (int mi = 0; mi < 4; mi++) cs[mi] = sa_cur[mi] * swv;
+            }
 #pragma unroll
             for (int mi = 0; mi < 4; mi++)
 #pragma unroll
@@ -390,7 +437,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         }
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa_nxt[mi];
-        sw_cur = sw_nxt;
+        swA = swA_n;
+        swB = swB_n;
     }
 
     // Epilogue: lane holds C[m][n .. n+3] of each subtile; rows outside [m0, mend) are not stored.
@@ -399,25 +447,63 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
         if (m < mend) {
 #pragma unroll
-            for (int ni = 0; ni < 8; ni++) {
-                const int64_t n = n0 + wn * 128 + ni * 16 + 4 * (lane >> 4);
+            for (int ni = 0; ni < NSUB; ni++) {
+                const int64_t n = nw0 + ni * 16 + 4 * (lane >> 4);
                 if (n < N) store4<OUT_BF16>(c, m * N + n, acc[ni][mi]);
             }
         }
     }
 }
 
+// Tile width for the dense large-M kernel: among 32 NSUB with NSUB = 6, 7, 8, the one with the least
+// (rounds of CUs) x (tile width), i.e. the least work per CU including the idle part of the last round,
+// with narrower tiles charged for their extra operand traffic per flop (half their width deficit,
+// measured: 4096 x 18432 runs best at 256, 4096 x 7168 at 224).
+int choose_nsub(int64_t M, int64_t N, int64_t ncu) {
+    int best = 8;
+    double best_cost = 0.0;
+    for (int ns = 8; ns >= 6; ns--) {
+        const int64_t bn = 32 * ns;
+        const int64_t tiles = ((M + kBig - 1) / kBig) * ((N + bn - 1) / bn);
+        const double cost = (double)((tiles + ncu - 1) / ncu) * (double)bn * (1.0 + 0.5 * (256.0 - bn) / 256.0);
+        if (ns == 8 || cost < best_cost * 0.999) {
+            best = ns;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+template <bool OUT_BF16, bool GROUPED, int NSUB>
+hipError_t launch_256_n(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
+                        int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
+    constexpr int64_t BN = 32 * NSUB;
+    const int64_t n_ntiles = (N + BN - 1) / BN;
+    int64_t n_mtiles, blocks;
+    if (GROUPED) {
+        // Every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at most
+        // len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tile rows cover all experts.
+        n_mtiles = M / kBig + (E + 1) / 2;
+        blocks = n_mtiles * n_ntiles;
+    } else {
+        n_mtiles = (M + kBig - 1) / kBig;
+        // supergroups of 16 x 16 tiles, 256 workgroups each (indices outside the grid exit at once)
+        blocks = ((n_mtiles + 15) / 16) * ((n_ntiles + 15) / 16) * 256;
+    }
+    gemm_bs_256_kernel<OUT_BF16, GROUPED, NSUB>
+        <<<dim3((unsigned)blocks), 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles);
+    return hipGetLastError();
+}
+
 template <bool OUT_BF16, bool GROUPED>
 hipError_t launch_256(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
                       int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
-    // Grouped: every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at
-    // most len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tiles cover all experts.
-    const int64_t n_mtiles = GROUPED ? M / kBig + (E + 1) / 2 : (M + kBig - 1) / kBig;
-    const int64_t n_tiles = n_mtiles * ((N + kBig - 1) / kBig);
-    const int64_t blocks = n_tiles;
-    gemm_bs_256_kernel<OUT_BF16, GROUPED>
-        <<<dim3((unsigned)blocks), 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_tiles);
-    return hipGetLastError();
+    const int nsub = GROUPED ? 8 : choose_nsub(M, N, cu_count());
+    switch (nsub) {
+        case 6: return launch_256_n<OUT_BF16, GROUPED, 6>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
+        case 7: return launch_256_n<OUT_BF16, GROUPED, 7>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
+        default: return launch_256_n<OUT_BF16, GROUPED, 8>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
+    }
 }
 
 // =============================================================================================

@@ -202,3 +202,25 @@ def test_grouped_full_moe_sampled():
     pad = r.row_token < 0
     assert np.all(c[pad] == 0.0)
     say(f"  max err/bound {ratio:.3g}")
+
+
+@pytest.mark.parametrize("M,N,K", [(2304, 7168, 256), (4096, 7168, 256), (300, 640, 1024)],
+                         ids=["width256", "width224", "width192"])
+def test_large_m_tile_widths(M, N, K):
+    """Shapes for which the large-M kernel picks each of its tile widths (256, 224, 192 weight rows; the
+    narrower ones have waves whose weight rows straddle a 128-row scale block)."""
+    g = np.random.default_rng(M + N)
+    a = g.standard_normal((M, K)).astype(np.float32)
+    w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w *= np.kron(np.exp2(g.integers(-3, 4, size=(N // 128, K // 128))), np.ones((128, 128))).astype(np.float32)
+    ab, wb = wl.bf16_bits(a), wl.bf16_bits(w)
+    say(f"gemm tile widths: M={M} N={N} K={K}")
+    c = gemm_out_to_f64(gpu_path(ab, wb, "f32"))
+    qa, sa = oracle.quant_act_1x128(ab)
+    qw, sw = oracle.quant_w_128x128(wb)
+    rows = sample_rows(M, 12, 5)
+    cols = np.unique(np.concatenate([sample_rows(N, 24, 6), np.arange(0, N, 32)]))  # every 32nd column too
+    C, B = oracle.gemm_blockscaled(qa, sa, qw, sw, rows=rows)
+    assert_gemm_within_bound(c[rows], C, B, False, f"{M}x{N} rows")
+    C, B = oracle.gemm_blockscaled(qa, sa, qw, sw, cols=cols)
+    assert_gemm_within_bound(c[:, cols], C, B, False, f"{M}x{N} cols")
