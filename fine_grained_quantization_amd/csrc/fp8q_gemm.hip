@@ -222,8 +222,10 @@ __global__ __launch_bounds__(256, 2) void gemm_blockscaled_kernel(const uint8_t 
 // x 2 along N, 64 tokens x 16 NSUB weight rows per wave, so 2 waves share each SIMD and one wave's promotion
 // VALU work overlaps the other's MFMAs.  Global tiles go straight to LDS with buffer loads (no staging
 // registers, K-block offset in a scalar register, rows past the end of the tile's range read as zeros);
-// 2 LDS stages of (256 + BN) x 128 B.  The host picks BN so that the number of tiles fills whole rounds of
-// the CUs as far as possible.
+// 2 LDS stages of (256 + BN) x 128 B plus the K-block's 256 activation scales and the weight scales of the
+// (at most 3) 128-row blocks the tile touches, which travel with the tiles so that no load has to be waited
+// for anywhere but at the stage barrier.  The host picks BN so that the number of tiles fills whole rounds
+// of the CUs as far as possible.
 // =============================================================================================
 
 constexpr int kBig = 256;  // tile rows along M
@@ -250,13 +252,31 @@ template <int BN>
 struct TileLoader {
     static constexpr int kWGroups = BN / 8;               // 8-row groups of the weight tile
     static constexpr int kWPerWave = (kWGroups + 7) / 8;  // groups per wave (the last may be partial)
-    i32x4 ra, rw;             // resources: this tile's A rows / W rows
+    // Scale area of a stage, 8 x 256 B, one dword per lane of each wave's single scale copy: waves 0-3 copy
+    // the activation scales of tile rows [64 w, 64 w + 64) (rows past the tile's last row read zeros), so
+    // that row r sits at float r; waves 4-7 each copy the weight scales of blocks nb0, nb0 + 1, nb0 + 2
+    // (clamped to the last block) into floats 256 + 64 (w - 4) + i.  The readers use wave 4's copy.
+    static constexpr int kScOff = (kBig + BN) * 128;
+    static constexpr int kStageBytes = kScOff + 8 * 256;
+    i32x4 ra, rw, rsw;        // resources: this tile's A rows / W rows / the weight scales
     int avoff[4];             // A: row * K + chunk * 16 for the wave's 4 instructions
     int wvoff[kWPerWave];     // W: same for the wave's weight row groups
+    int scvoff;               // this lane's scale offset (K-block 0)
+    const float *sa_tile;     // activation scales of the tile's first row in K-block 0
+    uint64_t sa_bytes;        // bytes of scales that belong to the tile's rows
+    int64_t M;
     __device__ __forceinline__ void init(const uint8_t *a_rows, uint64_t a_bytes, const uint8_t *w_rows,
-                                         uint64_t w_bytes, int64_t K, int wave, int lane) {
+                                         uint64_t w_bytes, int64_t K, int wave, int lane, const float *sa_tile_,
+                                         int64_t rows, int64_t M_, const float *sw_mat, int64_t NB, int64_t nb0) {
         ra = make_rsrc(a_rows, a_bytes);
         rw = make_rsrc(w_rows, w_bytes);
+        const int64_t KB = K >> 7;
+        rsw = make_rsrc(sw_mat, (uint64_t)NB * (uint64_t)KB * 4);
+        const int64_t nb = nb0 + lane < NB - 1 ? nb0 + lane : NB - 1;
+        scvoff = wave < 4 ? (wave * 64 + lane) * 4 : (lane < 3 ? (int)(nb * KB * 4) : kOutOfRange);
+        sa_tile = sa_tile_;
+        sa_bytes = (uint64_t)(rows < kBig ? rows : kBig) * 4;
+        M = M_;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int r = wave * 32 + j * 8 + (lane >> 3);
@@ -268,7 +288,13 @@ struct TileLoader {
             wvoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
         }
     }
-    __device__ __forceinline__ void issue(uint8_t *stage, int koff, int wave) const {
+    // Copies K-block kb (or, for koff == kOutOfRange, nothing) into `stage`; the scales of K-block ks
+    // (kb, clamped to the last block) come along, one dword per lane from in-bounds addresses.
+    __device__ __forceinline__ void issue(uint8_t *stage, int koff, int64_t ks, int wave) const {
+        const bool act = wave < 4;  // wave-uniform: the resource and offset are scalar selects
+        const i32x4 rs = act ? make_rsrc(sa_tile + ks * M, sa_bytes) : rsw;
+        fp8q_raw_buffer_load_lds(rs, (lds_ptr)(stage + kScOff + wave * 256), 4, scvoff, act ? 0 : (int)(ks * 4), 0,
+                                 0);
 #pragma unroll
         for (int j = 0; j < 4; j++)
             fp8q_raw_buffer_load_lds(ra, (lds_ptr)(stage + (wave * 32 + j * 8) * 128), 16, avoff[j], koff, 0, 0);
@@ -296,26 +322,23 @@ __device__ __forceinline__ bool supergroup_tile(int64_t t, int64_t n_mt, int64_t
     return mt < n_mt && nt < n_nt;
 }
 
+// One 256 x (32 NSUB) output tile, number t of a grid of n_mtiles x n_ntiles tiles whose columns start at
+// n_begin (dense), or of the expert-by-expert enumeration (grouped).  stage0 / stage1 are the workgroup's
+// two LDS stages, each at least TileLoader<32 NSUB>::kStageBytes.
 template <bool OUT_BF16, bool GROUPED, int NSUB>
-__global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
-                                                             const float *__restrict__ sa,
-                                                             const uint8_t *__restrict__ qw,
-                                                             const float *__restrict__ sw, void *__restrict__ c,
-                                                             int64_t M, int64_t N, int64_t K,
-                                                             const int32_t *__restrict__ off, int64_t E,
-                                                             int64_t n_mtiles, int64_t n_ntiles) {
+__device__ __forceinline__ void bs256_tile(uint8_t *stage0, uint8_t *stage1, const uint8_t *__restrict__ qa,
+                                           const float *__restrict__ sa, const uint8_t *__restrict__ qw,
+                                           const float *__restrict__ sw, void *__restrict__ c, int64_t M, int64_t N,
+                                           int64_t K, const int32_t *__restrict__ off, int64_t E, int64_t t,
+                                           int64_t n_begin, int64_t n_mtiles, int64_t n_ntiles) {
     constexpr int BN = 32 * NSUB;
     constexpr int WN = 16 * NSUB;  // weight rows per wave
-    constexpr int kStageBytes = (kBig + BN) * 128;
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;  // wave-uniform (scalar), 0 .. 7
     const int wm = wave & 3;   // 64-token quarter of the tile
     const int wn = wave >> 2;  // weight-row half of the tile
     const int64_t KB = K >> 7;
-    const int64_t t = blockIdx.x;
 
     int64_t m0, mend, n0;
     const uint8_t *W = qw;
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         int64_t mt, nt;
         if (!supergroup_tile(t, n_mtiles, n_ntiles, mt, nt)) return;
         m0 = mt * kBig;
-        n0 = nt * BN;
+        n0 = n_begin + nt * BN;
         mend = M;
     } else {
         // Tiles are enumerated expert by expert: expert e owns ceil(len_e / 256) M tiles of its segment.
@@ -349,28 +372,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         W = qw + e * N * K;
         SW = sw + e * (N / 128) * KB;
     }
-    const int64_t Mlast = mend - 1;
+    // Scales: the stage holds the activation scales of the tile's 256 rows and the weight scales of blocks
+    // nb0, nb0 + 1, nb0 + 2 (the tile's weight rows start in block nb0 and span at most 3 blocks).  The
+    // wave's weight rows start at nw0; subtiles ni < nib lie in block nbA, the others in nbA + 1 (a 16-row
+    // subtile never straddles a 128-row block).  With NSUB = 8 the waves are aligned to whole blocks and
+    // only nbA is used.
+    const int64_t nb0 = n0 / 128;
+    const int64_t nw0 = n0 + wn * WN;
+    const int nbA = (int)(nw0 / 128 - nb0);  // 0 .. 2
+    const int nbB = nbA + 1 < 2 ? nbA + 1 : 2;
+    const int nib = (int)((128 * (nw0 / 128 + 1) - nw0) / 16);
     TileLoader<BN> ld;
     ld.init(qa + m0 * K, (uint64_t)(mend - m0) * (uint64_t)K, W + n0 * K, (uint64_t)(N - n0) * (uint64_t)K, K,
-            wave, lane);
-
-    // Scales: this lane's 4 tokens (one per 16-row subtile).  The wave's weight rows start at nw0; subtiles
-    // ni < nib lie in scale block nbA, the others in nbA + 1 (a 16-row subtile never straddles a 128-row
-    // block).  With NSUB = 8 the waves are aligned to whole blocks and only nbA is used.
-    int64_t mrow[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++) {
-        const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
-        mrow[mi] = m < Mlast ? m : Mlast;
-    }
-    const int64_t nw0 = n0 + wn * WN;
-    const int64_t NBmax = N / 128 - 1;
-    int64_t nbA = nw0 / 128;
-    nbA = nbA < NBmax ? nbA : NBmax;
-    const int64_t nbB = nbA + 1 < NBmax ? nbA + 1 : NBmax;
-    const int nib = (int)((128 * (nw0 / 128 + 1) - nw0) / 16);
-    const float *swA_row = SW + nbA * KB;
-    const float *swB_row = SW + nbB * KB;
+            wave, lane, sa + m0, mend - m0, M, SW, N / 128, nb0);
 
     v4f acc[NSUB][4];
 #pragma unroll
@@ -378,11 +392,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) acc[ni][mi] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    ld.issue(stage0, 0, wave);
-    float sa_cur[4], sa_nxt[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa[mrow[mi]];
-    float swA = swA_row[0], swB = swB_row[0], swA_n = 0.f, swB_n = 0.f;
+    ld.issue(stage0, 0, 0, wave);
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
     for (int64_t kb = 0; kb < KB; kb++) {
@@ -391,19 +401,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         // This K-block's tiles have landed (own loads), and every wave is done with the other stage.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        {
-            // The prefetch is unconditional (past the last K-block it reads nothing and yields zeros), so
-            // the loop body is a single basic block.
-            const int64_t kn = kb + 1 < KB ? kb + 1 : kb;
-            ld.issue(nxt, kb + 1 < KB ? (int)((kb + 1) * 128) : kOutOfRange, wave);
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++) sa_nxt[mi] = sa[kn * M + mrow[mi]];
-            swA_n = swA_row[kn];
-            swB_n = swB_row[kn];
-        }
-        float csA[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) csA[mi] = sa_cur[mi] * swA;
+        // The prefetch is unconditional (past the last K-block it copies no tiles and yields zeros), so
+        // the loop body is a single basic block.
+        ld.issue(nxt, kb + 1 < KB ? (int)((kb + 1) * 128) : kOutOfRange, kb + 1 < KB ? kb + 1 : kb, wave);
         // The first weight fragment is read before the activation fragments so that the first MFMA waits
         // for two LDS reads, not five.  The fragment of weight subtile ni+1 is read while the 4 MFMAs of
         // subtile ni run; their partials are promoted right after issue (the first MFMA has finished by
@@ -413,6 +413,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         v8i af[4];
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) af[mi] = load_frag(cur, wm * 64 + mi * 16, lane);
+        // Scales (needed from the first promotion on) of tokens wm * 64 + mi * 16 + (lane & 15).
+        const float *sc = reinterpret_cast<const float *>(cur + TileLoader<BN>::kScOff);
+        float sa_cur[4], csA[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sc[wm * 64 + mi * 16 + (lane & 15)];
+        const float swA = sc[256 + nbA], swB = sc[256 + nbB];
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++) csA[mi] = sa_cur[mi] * swA;
 #pragma unroll
         for (int ni = 0; ni < NSUB; ni++) {
             v8i wf_next = wf;
@@ -435,10 +443,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
                 for (int r = 0; r < 4; r++) acc[ni][mi][r] = __builtin_fmaf(p[mi][r], cs[mi], acc[ni][mi][r]);
             wf = wf_next;
         }
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa_nxt[mi];
-        swA = swA_n;
-        swB = swB_n;
     }
 
     // Epilogue: lane holds C[m][n .. n+3] of each subtile; rows outside [m0, mend) are not stored.
@@ -455,55 +459,152 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
     }
 }
 
-// Tile width for the dense large-M kernel: among 32 NSUB with NSUB = 6, 7, 8, the one with the least
-// (rounds of CUs) x (tile width), i.e. the least work per CU including the idle part of the last round,
-// with narrower tiles charged for their extra operand traffic per flop (half their width deficit,
-// measured: 4096 x 18432 runs best at 256, 4096 x 7168 at 224).
-int choose_nsub(int64_t M, int64_t N, int64_t ncu) {
-    int best = 8;
-    double best_cost = 0.0;
+// Large-M GEMM.  Workgroups [0, main_blocks) cover columns [0, n_tail) with 256 x (32 NSUB) tiles; when
+// NSUB_TAIL != 0 the workgroups after them cover columns [n_tail, N) with narrower 256 x (32 NSUB_TAIL) tiles,
+// which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of the
+// last round.
+template <bool OUT_BF16, bool GROUPED, int NSUB, int NSUB_TAIL>
+__global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
+                                                             const float *__restrict__ sa,
+                                                             const uint8_t *__restrict__ qw,
+                                                             const float *__restrict__ sw, void *__restrict__ c,
+                                                             int64_t M, int64_t N, int64_t K,
+                                                             const int32_t *__restrict__ off, int64_t E,
+                                                             int64_t n_mtiles, int64_t n_ntiles, int64_t main_blocks,
+                                                             int64_t n_tail, int64_t n_ntiles_tail) {
+    constexpr int kMain = TileLoader<32 * NSUB>::kStageBytes;
+    constexpr int kTail = TileLoader<32 * (NSUB_TAIL ? NSUB_TAIL : NSUB)>::kStageBytes;
+    constexpr int kStageBytes = kMain > kTail ? kMain : kTail;
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+    const int64_t t = blockIdx.x;
+    if constexpr (NSUB_TAIL != 0) {
+        if (t >= main_blocks) {
+            bs256_tile<OUT_BF16, GROUPED, NSUB_TAIL>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, off, E,
+                                                      t - main_blocks, n_tail, n_mtiles, n_ntiles_tail);
+            return;
+        }
+    }
+    bs256_tile<OUT_BF16, GROUPED, NSUB>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, off, E, t, 0, n_mtiles,
+                                        n_ntiles);
+}
+
+// Launch plan of the dense large-M kernel: main tile width 32 ns over columns [0, n_tail), then (ns_tail != 0)
+// tiles of width 32 ns_tail over [n_tail, N).
+struct Plan256 {
+    int ns, ns_tail;
+    int64_t n_tail;
+};
+
+// Relative cost of one tile of width bn: its width, with narrower tiles charged for their extra operand
+// traffic per flop (half their width deficit; measured: 4096 x 18432 runs best at 256 wide, 4096 x 7168 at
+// 224).
+static double tile_cost(int64_t bn) { return (double)bn * (1.0 + 0.5 * (256.0 - (double)bn) / 256.0); }
+
+// Finishing time of tm tiles of cost a followed by t2 tiles of cost b on ncu CUs, each CU taking the next
+// tile as it becomes free (the dispatcher's order).
+static double makespan(int64_t tm, double a, int64_t t2, double b, int64_t ncu) {
+    const int64_t R = tm / ncu, rem = tm % ncu;
+    const double t1 = (double)R * a;                 // ncu - rem CUs are free from here
+    const double t2e = rem ? (double)(R + 1) * a : t1;  // the other rem CUs from here
+    if (t2 == 0) return t2e;
+    const int64_t early = ncu - rem;
+    const int64_t k = rem ? (int64_t)(a / b) : 0;  // tail tiles an early CU finishes before t2e
+    const int64_t done = t2 < early * k ? t2 : early * k;
+    const int64_t left = t2 - done;
+    if (left == 0) {
+        const double e = t1 + (double)((done + early - 1) / early) * b;
+        return e > t2e ? e : t2e;
+    }
+    const double base = t1 + (double)k * b > t2e ? t1 + (double)k * b : t2e;
+    return base + (double)((left + ncu - 1) / ncu) * b;
+}
+
+Plan256 plan_256(int64_t M, int64_t N, int64_t ncu) {
+    const int64_t n_mt = (M + kBig - 1) / kBig;
+    Plan256 best{8, 0, N};
+    double best_cost = -1.0;
     for (int ns = 8; ns >= 6; ns--) {
         const int64_t bn = 32 * ns;
-        const int64_t tiles = ((M + kBig - 1) / kBig) * ((N + bn - 1) / bn);
-        const double cost = (double)((tiles + ncu - 1) / ncu) * (double)bn * (1.0 + 0.5 * (256.0 - bn) / 256.0);
-        if (ns == 8 || cost < best_cost * 0.999) {
-            best = ns;
+        const int64_t n_nt = (N + bn - 1) / bn;
+        const double a = tile_cost(bn);
+        double cost = makespan(n_mt * n_nt, a, 0, 0.0, ncu);
+        Plan256 p{ns, 0, N};
+        // Split: as many whole tile columns as fill whole rounds, the rest in narrower tiles.
+        const int64_t T = n_mt * n_nt;
+        const int64_t cols = (T / ncu) * ncu / n_mt;
+        if (T % ncu != 0 && cols >= 1 && cols < n_nt) {
+            const int64_t n_split = cols * bn;
+            for (int nt : {4, 6}) {
+                const int64_t bnt = 32 * nt;
+                const int64_t t2 = n_mt * ((N - n_split + bnt - 1) / bnt);
+                const double c2 = makespan(n_mt * cols, a, t2, tile_cost(bnt), ncu);
+                if (c2 < cost * 0.98) {
+                    cost = c2;
+                    p = Plan256{ns, nt, n_split};
+                }
+            }
+        }
+        if (best_cost < 0.0 || cost < best_cost * 0.999) {
+            best = p;
             best_cost = cost;
         }
     }
     return best;
 }
 
-template <bool OUT_BF16, bool GROUPED, int NSUB>
-hipError_t launch_256_n(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
-                        int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
-    constexpr int64_t BN = 32 * NSUB;
-    const int64_t n_ntiles = (N + BN - 1) / BN;
-    int64_t n_mtiles, blocks;
-    if (GROUPED) {
-        // Every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at most
-        // len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tile rows cover all experts.
-        n_mtiles = M / kBig + (E + 1) / 2;
-        blocks = n_mtiles * n_ntiles;
-    } else {
-        n_mtiles = (M + kBig - 1) / kBig;
-        // supergroups of 16 x 16 tiles, 256 workgroups each (indices outside the grid exit at once)
-        blocks = ((n_mtiles + 15) / 16) * ((n_ntiles + 15) / 16) * 256;
+// Workgroups of a dense n_mt x n_nt grid in supergroup order (16 x 16 squares; indices outside the grid exit).
+static int64_t supergroup_blocks(int64_t n_mt, int64_t n_nt) { return ((n_mt + 15) / 16) * ((n_nt + 15) / 16) * 256; }
+
+template <bool OUT_BF16, int NSUB, int NSUB_TAIL>
+hipError_t launch_256_dense(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                            int64_t M, int64_t N, int64_t K, int64_t n_tail, hipStream_t stream) {
+    const int64_t n_mt = (M + kBig - 1) / kBig;
+    const int64_t n_nt = (n_tail + 32 * NSUB - 1) / (32 * NSUB);
+    const int64_t main_blocks = supergroup_blocks(n_mt, n_nt);
+    int64_t n_nt_tail = 0, blocks = main_blocks;
+    if (NSUB_TAIL != 0) {
+        n_nt_tail = (N - n_tail + 32 * NSUB_TAIL - 1) / (32 * NSUB_TAIL);
+        blocks += supergroup_blocks(n_mt, n_nt_tail);
     }
-    gemm_bs_256_kernel<OUT_BF16, GROUPED, NSUB>
-        <<<dim3((unsigned)blocks), 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles);
+    gemm_bs_256_kernel<OUT_BF16, false, NSUB, NSUB_TAIL><<<dim3((unsigned)blocks), 512, 0, stream>>>(
+        qa, sa, qw, sw, c, M, N, K, nullptr, 0, n_mt, n_nt, main_blocks, n_tail, n_nt_tail);
     return hipGetLastError();
 }
 
-template <bool OUT_BF16, bool GROUPED>
-hipError_t launch_256(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
-                      int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
-    const int nsub = GROUPED ? 8 : choose_nsub(M, N, cu_count());
-    switch (nsub) {
-        case 6: return launch_256_n<OUT_BF16, GROUPED, 6>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
-        case 7: return launch_256_n<OUT_BF16, GROUPED, 7>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
-        default: return launch_256_n<OUT_BF16, GROUPED, 8>(qa, sa, qw, sw, c, M, N, K, off, E, stream);
+template <bool OUT_BF16, int NSUB>
+hipError_t launch_256_dense_t(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                              int64_t M, int64_t N, int64_t K, const Plan256 &p, hipStream_t stream) {
+    switch (p.ns_tail) {
+        case 4: return launch_256_dense<OUT_BF16, NSUB, 4>(qa, sa, qw, sw, c, M, N, K, p.n_tail, stream);
+        case 6: return launch_256_dense<OUT_BF16, NSUB, 6>(qa, sa, qw, sw, c, M, N, K, p.n_tail, stream);
+        default: return launch_256_dense<OUT_BF16, NSUB, 0>(qa, sa, qw, sw, c, M, N, K, N, stream);
     }
+}
+
+template <bool OUT_BF16>
+hipError_t launch_256(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
+                      int64_t N, int64_t K, hipStream_t stream) {
+    const Plan256 p = plan_256(M, N, cu_count());
+    switch (p.ns) {
+        case 6: return launch_256_dense_t<OUT_BF16, 6>(qa, sa, qw, sw, c, M, N, K, p, stream);
+        case 7: return launch_256_dense_t<OUT_BF16, 7>(qa, sa, qw, sw, c, M, N, K, p, stream);
+        default: return launch_256_dense_t<OUT_BF16, 8>(qa, sa, qw, sw, c, M, N, K, p, stream);
+    }
+}
+
+template <bool OUT_BF16>
+hipError_t launch_256_grouped(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
+                              int64_t M, int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
+    constexpr int64_t BN = 256;
+    const int64_t n_ntiles = (N + BN - 1) / BN;
+    // Every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at most
+    // len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tile rows cover all experts.
+    const int64_t n_mtiles = M / kBig + (E + 1) / 2;
+    const int64_t blocks = n_mtiles * n_ntiles;
+    gemm_bs_256_kernel<OUT_BF16, true, 8, 0><<<dim3((unsigned)blocks), 512, 0, stream>>>(
+        qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0);
+    return hipGetLastError();
 }
 
 // =============================================================================================
@@ -737,15 +838,15 @@ hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uin
         return out_bf16 ? launch_smallm<true>(qa, sa, qw, sw, c, M, N, K, stream)
                         : launch_smallm<false>(qa, sa, qw, sw, c, M, N, K, stream);
     if (M <= 128) return launch<false>(qa, sa, qw, sw, c, out_bf16, M, N, K, nullptr, 0, stream);
-    return out_bf16 ? launch_256<true, false>(qa, sa, qw, sw, c, M, N, K, nullptr, 0, stream)
-                    : launch_256<false, false>(qa, sa, qw, sw, c, M, N, K, nullptr, 0, stream);
+    return out_bf16 ? launch_256<true>(qa, sa, qw, sw, c, M, N, K, stream)
+                    : launch_256<false>(qa, sa, qw, sw, c, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
                                            void *c, bool out_bf16, const int32_t *off, int64_t E, int64_t M_total,
                                            int64_t N, int64_t K, hipStream_t stream) {
-    return out_bf16 ? launch_256<true, true>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream)
-                    : launch_256<false, true>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream);
+    return out_bf16 ? launch_256_grouped<true>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream)
+                    : launch_256_grouped<false>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream);
 }
 
 }  // namespace fp8q

@@ -204,11 +204,15 @@ def test_grouped_full_moe_sampled():
     say(f"  max err/bound {ratio:.3g}")
 
 
-@pytest.mark.parametrize("M,N,K", [(2304, 7168, 256), (4096, 7168, 256), (300, 640, 1024)],
-                         ids=["width256", "width224", "width192"])
+@pytest.mark.parametrize("M,N,K", [(2304, 7168, 256), (2048, 7168, 256), (300, 640, 1024), (4096, 7168, 256),
+                                   (1024, 18432, 256)],
+                         ids=["w256", "w224", "w192", "w256+tail192", "w192+tail128"])
 def test_large_m_tile_widths(M, N, K):
-    """Shapes for which the large-M kernel picks each of its tile widths (256, 224, 192 weight rows; the
-    narrower ones have waves whose weight rows straddle a 128-row scale block)."""
+    """Shapes for which the large-M kernel's launch plan takes each of its tile widths: 256, 224 and 192
+    weight rows alone, and 256 (192) wide tiles over the leading columns followed by 192 (128) wide tiles over
+    the rest, starting at column 4096 (12288).  The narrower widths have waves whose weight rows straddle a
+    128-row scale block, and the tail tiles start at columns that are not multiples of 128 rows' blocks of
+    the main width."""
     g = np.random.default_rng(M + N)
     a = g.standard_normal((M, K)).astype(np.float32)
     w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
