@@ -614,14 +614,14 @@ hipError_t launch_256_grouped(const uint8_t *qa, const float *sa, const uint8_t 
 // For each of its K-blocks a wave copies the slice's weight rows and the 64 activation rows, as whole
 // 128-byte lines, straight into its own LDS slot (buffer loads into LDS), waits, and multiplies them with
 // MFMAs (NSUB = ceil(R / 16) weight subtiles x 4 token subtiles), promoting each partial with its scales.
-// With 8 waves per CU, 8 K-blocks per CU are in flight.  The 8 partial sums are then added through LDS
-// in a fixed tree order (deterministic) and wave 0 stores the slice.  Every load is unconditional:
-// rows past the slice or past M and K-blocks past the end read zeros.
+// With 8 waves per CU, 8 K-blocks per CU are in flight.  The 8 partial sums then go to LDS, and each wave
+// adds up (in wave order, so deterministically) and stores an eighth of the slice's outputs.  Every load is
+// unconditional: rows past the slice or past M and K-blocks past the end read zeros.
 // =============================================================================================
 
 constexpr int kSmallM = 64;
 constexpr int kDecWaves = 8;
-constexpr int kDecMaxSub = 5;  // LDS: 8 waves x (5 x 2 KB weight + 8 KB activation) = 144 KB
+constexpr int kDecMaxSub = 5;  // LDS: 8 waves x (5 x 2 KB weight + 8 KB activation) = 144 KB, 8 x 20 KB partials
 
 template <bool OUT_BF16, int NSUB>
 __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__restrict__ qa,
@@ -631,8 +631,10 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
                                                              int64_t M, int64_t N, int64_t K, int64_t rows_per_wg) {
     constexpr int kW = NSUB * 16 * 128;
     constexpr int kA = kSmallM * 128;
-    constexpr int kSlotBytes = kW + kA;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDecWaves * kSlotBytes];
+    constexpr int kSlotBytes = kW + kA + 512;  // + the K-block's 64 token scales and 64 weight-scale slots
+    constexpr int kPart = NSUB * 4 * 64 * 16;  // one wave's partial sums
+    constexpr int kLds = kDecWaves * kSlotBytes > kDecWaves * kPart ? kDecWaves * kSlotBytes : kDecWaves * kPart;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -660,20 +662,20 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
         const int r = 8 * j + rsub;
         w_voff[j] = r * (int)K + (((lane & 7) ^ swzf(r)) << 4);
     }
-    // Scales: token scale offsets per token subtile; this lane's weight rows 16 ns + 4 (lane / 16) .. +3 lie in
-    // one 128-row scale block (the slice start is a multiple of 8).
-    int s_voff[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++) {
-        const int tok = mi * 16 + (lane & 15);
-        s_voff[mi] = tok < M ? tok * 4 : kOutOfRange;
-    }
-    const float *sw_lane[NSUB];
+    // Scales travel with the K-block's copies: lane t copies token t's scale (tokens past M copy a scale
+    // that is never used, or zero past the end), lanes 0 and 1 copy the weight scales of blocks nb0 and
+    // nb0 + 1 (the slice spans at most two 128-row blocks), the other lanes zeros.  This lane's weight rows
+    // 16 ns + 4 (lane / 16) .. +3 lie in one block.
+    const int64_t nb0 = n0 / 128;
+    const i32x4 rSW = make_rsrc(sw, (uint64_t)(N / 128) * (uint64_t)KB * 4);
+    const int64_t nbl = nb0 + lane < N / 128 - 1 ? nb0 + lane : N / 128 - 1;
+    const int sw_voff = lane < 2 ? (int)(nbl * KB * 4) : kOutOfRange;
+    int sw_idx[NSUB];
 #pragma unroll
     for (int ns = 0; ns < NSUB; ns++) {
         int64_t nb = (n0 + ns * 16 + 4 * (lane >> 4)) / 128;
         nb = nb < N / 128 ? nb : N / 128 - 1;
-        sw_lane[ns] = sw + nb * KB;
+        sw_idx[ns] = (int)(nb - nb0);  // 0 or 1
     }
 
     v4f acc[NSUB][4];
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
     // Per K-block: wait for its copies, read all its fragments into registers, then start the copies of the
     // wave's next K-block into the (now free) slot, and only then run the MFMAs and promotions, which
     // overlap with those copies.
-    auto issue = [&](int kb, float (&s4)[4], float (&swv)[NSUB]) {
+    auto issue = [&](int kb) {
         const int so = kb < KB ? kb * 128 : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < 2 * NSUB; j++)
@@ -696,17 +698,15 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
         for (int j = 0; j < 8; j++)
             fp8q_raw_buffer_load_lds(rA, (__attribute__((address_space(3))) void *)(aslot + j * 1024), 16, a_voff[j],
                                      so, 0, 0);
-        const int sso = kb < KB ? kb * (int)M * 4 : kOutOfRange;
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) s4[mi] = fp8q_raw_buffer_load_f32(rS, s_voff[mi], sso, 0);
-        const int kbc = kb < KB ? kb : KB - 1;
-#pragma unroll
-        for (int ns = 0; ns < NSUB; ns++) swv[ns] = sw_lane[ns][kbc];
+        fp8q_raw_buffer_load_lds(rS, (__attribute__((address_space(3))) void *)(aslot + kA), 4, lane * 4,
+                                 kb < KB ? kb * (int)M * 4 : kOutOfRange, 0, 0);
+        fp8q_raw_buffer_load_lds(rSW, (__attribute__((address_space(3))) void *)(aslot + kA + 256), 4, sw_voff,
+                                 kb < KB ? kb * 4 : kOutOfRange, 0, 0);
     };
 
     const int NI = (KB + kDecWaves - 1) / kDecWaves;
-    float s4[4], swv[NSUB];
-    issue(wave, s4, swv);
+    issue(wave);
+    const float *ssl = reinterpret_cast<const float *>(aslot + kA);
     for (int i = 0; i < NI; i++) {
         __builtin_amdgcn_s_waitcnt(0);  // copies (and scales) of K-block wave + 8 i have landed
         v8i af[4], wf[NSUB];
@@ -714,13 +714,18 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
         for (int mi = 0; mi < 4; mi++) af[mi] = load_frag(aslot, mi * 16, lane);
 #pragma unroll
         for (int ns = 0; ns < NSUB; ns++) wf[ns] = load_frag(wslot, ns * 16, lane);
+        float s4[4], swv[NSUB];
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++) s4[mi] = ssl[mi * 16 + (lane & 15)];
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ns++) swv[ns] = ssl[64 + sw_idx[ns]];
         float cs[NSUB][4];
 #pragma unroll
         for (int ns = 0; ns < NSUB; ns++)
 #pragma unroll
             for (int mi = 0; mi < 4; mi++) cs[ns][mi] = s4[mi] * swv[ns];
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // fragments are in registers: the slot may be overwritten
-        issue(wave + kDecWaves * (i + 1), s4, swv);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // fragments and scales are in registers: the slot may be overwritten
+        issue(wave + kDecWaves * (i + 1));
 #pragma unroll
         for (int ns = 0; ns < NSUB; ns++) {
             v4f p[4];
@@ -734,41 +739,30 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last (out-of-range) copies have retired before the slot is reused
 
-    // Tree reduction of the 8 K-split partials through LDS (fixed order): waves [h, 2h) hand their partial
-    // to waves [0, h), for h = 4, 2, 1.  A partial is NSUB * 4 * 64 lanes * 16 bytes <= 20 KB.
-    constexpr int kPart = NSUB * 4 * 64 * 16;
+    // Reduction of the 8 K-split partials: once every wave is done with its slot, each writes its partial
+    // (NSUB x 4 subtile pairs) to LDS; then wave w sums pairs w, w + 8, w + 16 over the waves in order and
+    // stores them.
+    __syncthreads();
 #pragma unroll
-    for (int h = 4; h >= 1; h >>= 1) {
-        __syncthreads();
-        if (wave >= h && wave < 2 * h) {
-            uint8_t *dst = lds + (wave - h) * kPart;
+    for (int ns = 0; ns < NSUB; ns++)
 #pragma unroll
-            for (int ns = 0; ns < NSUB; ns++)
+        for (int mi = 0; mi < 4; mi++)
+            *reinterpret_cast<v4f *>(lds + wave * kPart + ((ns * 4 + mi) * 64 + lane) * 16) = acc[ns][mi];
+    __syncthreads();
 #pragma unroll
-                for (int mi = 0; mi < 4; mi++)
-                    *reinterpret_cast<v4f *>(dst + ((ns * 4 + mi) * 64 + lane) * 16) = acc[ns][mi];
-        }
-        __syncthreads();
-        if (wave < h) {
-            const uint8_t *src = lds + wave * kPart;
+    for (int q0 = 0; q0 < NSUB * 4; q0 += kDecWaves) {
+        const int q = q0 + wave;  // wave-uniform
+        if (q < NSUB * 4) {
+            v4f s = *reinterpret_cast<const v4f *>(lds + (q * 64 + lane) * 16);
 #pragma unroll
-            for (int ns = 0; ns < NSUB; ns++)
-#pragma unroll
-                for (int mi = 0; mi < 4; mi++) {
-                    const v4f v = *reinterpret_cast<const v4f *>(src + ((ns * 4 + mi) * 64 + lane) * 16);
-                    acc[ns][mi][0] += v[0]; acc[ns][mi][1] += v[1]; acc[ns][mi][2] += v[2]; acc[ns][mi][3] += v[3];
-                }
-        }
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int ns = 0; ns < NSUB; ns++) {
-            const int nl = ns * 16 + 4 * (lane >> 4);  // 4 rows nl .. nl+3 of the slice (all in or all out)
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++) {
-                const int64_t m = mi * 16 + (lane & 15);
-                if (m < M && nl < nrows) store4<OUT_BF16>(c, m * N + n0 + nl, acc[ns][mi]);
+            for (int w = 1; w < kDecWaves; w++) {
+                const v4f v = *reinterpret_cast<const v4f *>(lds + w * kPart + (q * 64 + lane) * 16);
+                s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
             }
+            const int ns = q >> 2, mi = q & 3;
+            const int nl = ns * 16 + 4 * (lane >> 4);  // 4 rows nl .. nl+3 of the slice (all in or all out)
+            const int64_t m = mi * 16 + (lane & 15);
+            if (m < M && nl < nrows) store4<OUT_BF16>(c, m * N + n0 + nl, s);
         }
     }
 }
