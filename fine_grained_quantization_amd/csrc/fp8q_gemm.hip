@@ -322,56 +322,80 @@ __device__ __forceinline__ bool supergroup_tile(int64_t t, int64_t n_mt, int64_t
     return mt < n_mt && nt < n_nt;
 }
 
-// One 256 x (32 NSUB) output tile, number t of a grid of n_mtiles x n_ntiles tiles whose columns start at
-// n_begin (dense), or of the expert-by-expert enumeration (grouped).  stage0 / stage1 are the workgroup's
-// two LDS stages, each at least TileLoader<32 NSUB>::kStageBytes.
-template <bool OUT_BF16, bool GROUPED, int NSUB>
-__device__ __forceinline__ void bs256_tile(uint8_t *stage0, uint8_t *stage1, const uint8_t *__restrict__ qa,
-                                           const float *__restrict__ sa, const uint8_t *__restrict__ qw,
-                                           const float *__restrict__ sw, void *__restrict__ c, int64_t M, int64_t N,
-                                           int64_t K, const int32_t *__restrict__ off, int64_t E, int64_t t,
-                                           int64_t n_begin, int64_t n_mtiles, int64_t n_ntiles) {
-    constexpr int BN = 32 * NSUB;
+// Coordinates of dense tile t (supergroup order over an n_mtiles x n_ntiles grid of 256 x bn tiles whose
+// columns start at n_begin).  Returns false for indices outside the grid.
+__device__ __forceinline__ bool dense_tile(int64_t t, int64_t n_begin, int64_t n_mtiles, int64_t n_ntiles, int64_t bn,
+                                           int64_t &m0, int64_t &n0) {
+    int64_t mt, nt;
+    if (!supergroup_tile(t, n_mtiles, n_ntiles, mt, nt)) return false;
+    m0 = mt * kBig;
+    n0 = n_begin + nt * bn;
+    return true;
+}
+
+// Coordinates of grouped tile t: tiles are enumerated expert by expert (expert e owns ceil(len_e / 256) M
+// tiles of its segment), tile T = mt * n_ntiles + nt with N fastest.  Workgroups are dealt to the 8 XCDs
+// round-robin; the permutation below gives XCD x the 32 consecutive tiles [256 r + 32 x, +32) of each round r
+// of 256, so the tiles sharing activation rows (and, mostly, an expert's weights) meet in one L2.  Returns
+// false past the last expert's tiles.
+__device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restrict__ off, int64_t E, int64_t M,
+                                             int64_t n_mtiles, int64_t n_ntiles, int64_t bn, int lane, int64_t &m0,
+                                             int64_t &mend, int64_t &n0, int64_t &e) {
+    const int64_t T = (t / 256) * 256 + (t % 8) * 32 + (t % 256) / 8;
+    const int64_t mt = T / n_ntiles;  // n_mtiles is an upper bound on the number of M tiles
+    if (mt >= n_mtiles) return false;
+    n0 = (T % n_ntiles) * bn;
+    // The expert owning M tile mt: a prefix sum of the experts' tile counts, 64 experts per pass (lane i
+    // holds expert base + i), and the first lane whose running total exceeds mt.
+    int64_t before = 0;
+    for (int64_t base = 0; base < E; base += 64) {
+        const int64_t i = base + lane;
+        int lo = 0, hi = 0, cnt = 0;
+        if (i < E) {
+            lo = off[i];
+            hi = off[i + 1];
+            cnt = hi > lo ? (hi - lo + kBig - 1) / kBig : 0;
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += u;
+        }
+        const uint64_t hit = __ballot(i < E && before + incl > mt);
+        if (hit) {
+            const int L = __builtin_ctzll(hit);
+            e = base + L;
+            const int lo_e = __shfl(lo, L, 64), hi_e = __shfl(hi, L, 64);
+            const int64_t first = before + __shfl(incl, L, 64) - __shfl(cnt, L, 64);
+            m0 = lo_e + (mt - first) * kBig;
+            mend = hi_e < M ? hi_e : M;
+            return true;
+        }
+        before += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
+// One output tile of (512 / WAVES_N) rows x (16 NSUB WAVES_N) weight rows starting at (m0, n0): 8 waves, 8 /
+// WAVES_N along M (64 tokens each) x WAVES_N along N (16 NSUB weight rows each).  WAVES_N = 2 is the 256-row
+// tile; WAVES_N = 4 (NSUB = 4) is the 128 x 256 tile for grouped segments with 128 rows left.  W / SW are the
+// weight matrix and its scales (an expert's, in the grouped case), and rows >= mend are not stored.
+// stage0 / stage1 are the workgroup's two LDS stages, each at least TileLoader<BN>::kStageBytes.
+template <bool OUT_BF16, int NSUB, int WAVES_N>
+__device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const uint8_t *__restrict__ qa,
+                                        const float *__restrict__ sa, const uint8_t *__restrict__ W,
+                                        const float *__restrict__ SW, void *__restrict__ c, int64_t M, int64_t N,
+                                        int64_t K, int64_t m0, int64_t mend, int64_t n0) {
+    constexpr int WM_WAVES = 8 / WAVES_N;
+    constexpr int BN = 16 * NSUB * WAVES_N;
     constexpr int WN = 16 * NSUB;  // weight rows per wave
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;  // wave-uniform (scalar), 0 .. 7
-    const int wm = wave & 3;   // 64-token quarter of the tile
-    const int wn = wave >> 2;  // weight-row half of the tile
+    const int wm = wave % WM_WAVES;  // 64-token slab of the tile
+    const int wn = wave / WM_WAVES;  // weight-row slab of the tile
     const int64_t KB = K >> 7;
-
-    int64_t m0, mend, n0;
-    const uint8_t *W = qw;
-    const float *SW = sw;
-    if (!GROUPED) {
-        int64_t mt, nt;
-        if (!supergroup_tile(t, n_mtiles, n_ntiles, mt, nt)) return;
-        m0 = mt * kBig;
-        n0 = n_begin + nt * BN;
-        mend = M;
-    } else {
-        // Tiles are enumerated expert by expert: expert e owns ceil(len_e / 256) M tiles of its segment.
-        // N is the fastest index here, so the workgroups resident together cover few experts and share
-        // both their weights and their activation rows in L2.
-        const int64_t mt = t / n_ntiles;  // n_mtiles is an upper bound on the number of M tiles
-        if (mt >= n_mtiles) return;
-        n0 = (t % n_ntiles) * BN;
-        int64_t before = 0, e = -1;
-        for (int64_t i = 0; i < E; i++) {
-            const int64_t lo = off[i], hi = off[i + 1];
-            const int64_t cnt = hi > lo ? (hi - lo + kBig - 1) / kBig : 0;
-            if (mt < before + cnt) {
-                e = i;
-                m0 = lo + (mt - before) * kBig;
-                mend = hi < M ? hi : M;
-                break;
-            }
-            before += cnt;
-        }
-        if (e < 0) return;  // beyond the last expert's tiles
-        W = qw + e * N * K;
-        SW = sw + e * (N / 128) * KB;
-    }
     // Scales: the stage holds the activation scales of the tile's 256 rows and the weight scales of blocks
     // nb0, nb0 + 1, nb0 + 2 (the tile's weight rows start in block nb0 and span at most 3 blocks).  The
     // wave's weight rows start at nw0; subtiles ni < nib lie in block nbA, the others in nbA + 1 (a 16-row
@@ -459,10 +483,11 @@ __device__ __forceinline__ void bs256_tile(uint8_t *stage0, uint8_t *stage1, con
     }
 }
 
-// Large-M GEMM.  Workgroups [0, main_blocks) cover columns [0, n_tail) with 256 x (32 NSUB) tiles; when
-// NSUB_TAIL != 0 the workgroups after them cover columns [n_tail, N) with narrower 256 x (32 NSUB_TAIL) tiles,
-// which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of the
-// last round.
+// Large-M GEMM.  Dense: workgroups [0, main_blocks) cover columns [0, n_tail) with 256 x (32 NSUB) tiles;
+// when NSUB_TAIL != 0 the workgroups after them cover columns [n_tail, N) with narrower 256 x (32 NSUB_TAIL)
+// tiles, which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of
+// the last round.  Grouped (NSUB = 8): one 256 x 256 tile per workgroup, or 128 x 256 where a segment has
+// only 128 rows left.
 template <bool OUT_BF16, bool GROUPED, int NSUB, int NSUB_TAIL>
 __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
                                                              const float *__restrict__ sa,
@@ -478,15 +503,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
     const int64_t t = blockIdx.x;
+    int64_t m0, mend = M, n0;
+    if constexpr (GROUPED) {
+        int64_t e = 0;
+        if (!grouped_tile(t, off, E, M, n_mtiles, n_ntiles, 32 * NSUB, threadIdx.x & 63, m0, mend, n0, e)) return;
+        const uint8_t *W = qw + e * N * K;
+        const float *SW = sw + e * (N / 128) * (K >> 7);
+        if (mend - m0 <= 128)  // a segment's last 128 rows: the 128 x 256 layout does no work on absent rows
+            bs_tile<OUT_BF16, 4, 4>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0);
+        else
+            bs_tile<OUT_BF16, NSUB, 2>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0);
+        return;
+    }
     if constexpr (NSUB_TAIL != 0) {
         if (t >= main_blocks) {
-            bs256_tile<OUT_BF16, GROUPED, NSUB_TAIL>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, off, E,
-                                                      t - main_blocks, n_tail, n_mtiles, n_ntiles_tail);
+            if (!dense_tile(t - main_blocks, n_tail, n_mtiles, n_ntiles_tail, 32 * NSUB_TAIL, m0, n0)) return;
+            bs_tile<OUT_BF16, NSUB_TAIL, 2>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, m0, M, n0);
             return;
         }
     }
-    bs256_tile<OUT_BF16, GROUPED, NSUB>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, off, E, t, 0, n_mtiles,
-                                        n_ntiles);
+    if (!dense_tile(t, 0, n_mtiles, n_ntiles, 32 * NSUB, m0, n0)) return;
+    bs_tile<OUT_BF16, NSUB, 2>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, m0, M, n0);
 }
 
 // Launch plan of the dense large-M kernel: main tile width 32 ns over columns [0, n_tail), then (ns_tail != 0)
@@ -601,7 +638,9 @@ hipError_t launch_256_grouped(const uint8_t *qa, const float *sa, const uint8_t 
     // Every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at most
     // len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tile rows cover all experts.
     const int64_t n_mtiles = M / kBig + (E + 1) / 2;
-    const int64_t blocks = n_mtiles * n_ntiles;
+    // whole rounds of 256 workgroups: the XCD permutation of the tile index is a bijection on each round,
+    // and the indices past the last tile exit at once
+    const int64_t blocks = (n_mtiles * n_ntiles + 255) / 256 * 256;
     gemm_bs_256_kernel<OUT_BF16, true, 8, 0><<<dim3((unsigned)blocks), 512, 0, stream>>>(
         qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0);
     return hipGetLastError();
