@@ -8,10 +8,13 @@ workload runs the grouped GEMM over expert segments.)
 
 Prints ONE JSON line.  `value` is the step's GEMM work divided by the whole step time (TFLOP/s), so the
 quantizers' time counts against it; the timed region is K back-to-back steps between two synchronizations.
-Per-kernel times come from a second pass of K steps with HIP events recorded on the stream the kernels are
-launched on, around every launch (events between launches add small gaps, so that pass is not used for
-`value`).  `roofline` describes the dominant kernel (the GEMM) against MI355X's published peaks;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+The GEMM's own duration is measured inside that region with a HIP event pair around each of its launches,
+recorded on the stream the kernels are launched on; the quantizers' durations come from a second pass of K
+steps with an event pair around every launch.  `roofline` describes the dominant kernel (the GEMM) against
+MI355X's published peaks; its `traffic` (HBM bytes per launch) is read from the committed rocprofv3
+summary of that kernel and workload under profiles/, and is null when the kernel sources have changed since
+the counters were taken (the summary records their SHA-256).  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 
 The decode workload's weight (132 MB) would fit in the 256 MB Infinity Cache, so the bench keeps four
 copies and rotates them step by step: every step streams its weight from HBM, as a model with many layers
@@ -131,11 +134,12 @@ class Workload:
             self.qw = self.qw_copies[self.step_count % len(self.qw_copies)]
         self.step_count += 1
         for i, (_, fn, _) in enumerate(self.kernels):
-            if events is not None:
-                events[i][0].record()
+            ev = events[i] if events is not None else None
+            if ev is not None:
+                ev[0].record()
             fn()
-            if events is not None:
-                events[i][1].record()
+            if ev is not None:
+                ev[1].record()
 
 
 def cpu_baseline(wk: Workload, target_s: float = 12.0):
@@ -181,6 +185,93 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
                       f"quantization of {what}, and the double-precision GEMM of those rows; {total:.1f} s"}
 
 
+class HipEvents:
+    """Timing events of the HIP runtime the process already uses (found in /proc/self/maps), created with
+    hipEventDisableSystemFence: recording one does not add a system-scope release, which keeps the gap
+    between an event and the kernel after it small."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+class _Rec:
+    """Event pair endpoint with the torch.cuda.Event record() interface, on the current stream."""
+
+    def __init__(self, he, ev):
+        self.he, self.ev = he, ev
+
+    def record(self):
+        import torch
+
+        self.he.record(self.ev, torch.cuda.current_stream().cuda_stream)
+
+
+GEMM_SOURCES = ("fine_grained_quantization_amd/csrc/fp8q_gemm.hip", "fine_grained_quantization_amd/csrc/fp8q_device.h")
+
+
+def sources_sha256(paths=GEMM_SOURCES):
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kname, workload):
+    """HBM bytes per launch of `kname` on `workload` from its committed rocprofv3 summary, or None when
+    there is none or the kernel sources differ from the ones it was taken with."""
+    path = os.path.join(ROOT, "profiles", f"{kname}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith(("source_sha256", "traffic_bytes_per_launch")):
+                k, v = line.strip().strip("`").split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != sources_sha256() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,20 +305,28 @@ def main():
         wk.step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, back to back, between two synchronizations.
+    # Timed region: exactly K steps, back to back, between two synchronizations; an event pair brackets
+    # every GEMM launch in it.
+    nk = len(wk.kernels)
+    he = HipEvents()
+    gemm_raw = [(he.create(), he.create()) for _ in range(args.steps)]
+    gemm_ev = [[_Rec(he, a), _Rec(he, b)] for a, b in gemm_raw]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        wk.step()
+        wk.step([None] * (nk - 1) + [gemm_ev[s]])
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(end) / args.steps
+    gemm_us = 1e3 * float(np.mean([he.elapsed_ms(a, b) for a, b in gemm_raw]))
+    for a, b in gemm_raw:
+        he.destroy(a)
+        he.destroy(b)
 
-    # Per-kernel durations: K more steps with an event pair around every launch.
-    nk = len(wk.kernels)
+    # Quantizer durations: K more steps with an event pair around every launch.
     events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(nk)]
               for _ in range(args.steps)]
     for s in range(args.steps):
@@ -236,7 +335,10 @@ def main():
 
     kernels = {}
     for i, (kname, _, work) in enumerate(wk.kernels):
-        us = 1e3 * float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+        if i == nk - 1:
+            us = gemm_us  # measured in the timed region
+        else:
+            us = 1e3 * float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
         info = {"us": round(us, 2)}
         if "flops" in work:
             info["TFLOP/s"] = round(work["flops"] / us / 1e6, 1)
@@ -247,12 +349,14 @@ def main():
 
     gname, _, gwork = wk.kernels[-1]
     g = kernels[gname]
+    traffic = profiled_traffic(gname, args.workload)
     if args.workload == "decode":
         roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"kernel": gname, "bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+    roof["algorithmic_bytes"] = int(gwork["bytes"])
 
     out = {
         "metric": METRIC,
