@@ -7,7 +7,9 @@ One step = the whole path over one batch of synthetic input already resident in 
 workload runs the grouped GEMM over expert segments.)
 
 Prints ONE JSON line.  `value` is the step's GEMM work divided by the whole step time (TFLOP/s), so the
-quantizers' time counts against it; the timed region is K back-to-back steps between two synchronizations.
+quantizers' time counts against it; the timed region is K back-to-back steps between two synchronizations,
+after an untimed settle phase (the step repeated for --settle-ms, reported as settle_steps) and W warmup
+steps.
 The GEMM's own duration is measured inside that region with a HIP event pair around each of its launches,
 recorded on the stream the kernels are launched on; the quantizers' durations come from a second pass of K
 steps with an event pair around every launch.  `roofline` describes the dominant kernel (the GEMM) against
@@ -279,6 +281,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="up", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warmup steps, repeat the step for this long (untimed) so that the GPU's "
+                         "clocks reach their sustained state; the count is reported as settle_steps")
     ap.add_argument("--pmc-copy-mb", type=int, default=0,
                     help="before warmup, run one plain elementwise copy (torch.neg) of this many MiB; its "
                          "FETCH_SIZE / WRITE_SIZE under rocprofv3 calibrate the traffic counters")
@@ -301,6 +306,15 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    # Settle: a few milliseconds of warmup leave the GPU below its sustained clock (measured: the up GEMM
+    # runs at 568 us after 5 steps, 490 us after 100), so repeat the step, untimed, for settle_ms first.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(4):
+            wk.step()
+        settle_steps += 4
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         wk.step()
     torch.cuda.synchronize()
@@ -365,6 +379,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
