@@ -370,7 +370,9 @@ __device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restric
             const int64_t first = before + __shfl(incl, L, 64) - __shfl(cnt, L, 64);
             m0 = lo_e + (mt - first) * kBig;
             mend = hi_e < M ? hi_e : M;
-            return true;
+            // offsets that break the layout rules (decreasing, negative, past M) yield no rows, never a
+            // range outside [0, M)
+            return m0 >= 0 && m0 < mend;
         }
         before += __shfl(incl, 63, 64);
     }

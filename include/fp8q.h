@@ -100,10 +100,10 @@ int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw,
  *         then produce exact zeros.
  *   c   : [M_total, N] bf16 or fp32.
  * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23.
- * The offsets live on the device and are not checked on the host; rows that no
- * segment covers (only possible when the offsets break the rules above) are
- * written as zeros, and every memory access stays inside the buffers described
- * by M_total, E, N and K. */
+ * The offsets live on the device and are not checked on the host.  When they
+ * break the rules above, rows that no segment covers are left unwritten (c keeps
+ * its previous contents there), and every memory access still stays inside the
+ * buffers described by M_total, E, N and K. */
 int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                                   int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
                                   int64_t K, void *stream);

@@ -179,6 +179,34 @@ def test_grouped_skewed_with_empty_expert(out):
         assert np.all(c[off[e] + cnt:off[e + 1]] == 0.0)
 
 
+def test_grouped_offsets_outside_the_rules():
+    """Offsets that break the layout rules (the header's promise for them): segments that end before
+    M_total leave the rows after them untouched, and a last offset past M_total is cut at M_total."""
+    K, N, M = 512, 256, 1024
+    g = np.random.default_rng(5)
+    ab = wl.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    wb = wl.bf16_bits((g.standard_normal((2, N, K)) * 0.02).astype(np.float32))
+    qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(ab))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(wb))
+    oqa, osa = oracle.quant_act_1x128(ab)
+    oqw, osw = oracle.quant_w_128x128(wb)
+    # segments [0, 384) and [384, 640) of a 1024-row buffer: rows 640.. keep the sentinel
+    say("grouped gemm: segments ending at 640 of 1024 rows")
+    off = np.array([0, 384, 640], np.int32)
+    c = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda(), out_dtype=torch.float32, c=c)
+    ch = gemm_out_to_f64(c)
+    assert np.all(ch[640:] == 7.0)
+    C, B = oracle.grouped_gemm_blockscaled(oqa[:640], osa[:, :640], oqw, osw, off)
+    assert_gemm_within_bound(ch[:640], C, B, False, "short segments")
+    # a last offset of 2048 for a 1024-row buffer: expert 1 covers rows [256, 1024)
+    say("grouped gemm: last offset 2048 for 1024 rows")
+    off = np.array([0, 256, 2048], np.int32)
+    c = fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda(), out_dtype=torch.float32)
+    C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, np.array([0, 256, M], np.int32))
+    assert_gemm_within_bound(gemm_out_to_f64(c), C, B, False, "offset past M_total")
+
+
 def test_grouped_full_moe_sampled():
     """The full MoE layer: 8192 tokens, top-8 of 64 experts, expert weights [2048, 7168]; sampled rows
     from every expert segment (first, last routed row and a random one), all 2048 columns."""
