@@ -69,6 +69,8 @@ def load(path: str | None = None):
         lib.oracle_gemm_blockscaled.restype = ctypes.c_int
         lib.oracle_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P, I64, P, P]
         lib.oracle_grouped_gemm_blockscaled.restype = ctypes.c_int
+        lib.oracle_dequant_w_128x128.argtypes = [P, P, I64, I64, P]
+        lib.oracle_dequant_w_128x128.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -215,3 +217,20 @@ def grouped_gemm_blockscaled(qa, sa, qw, sw, offsets, rows=None, cols=None, lib=
                                                _ptr(ms), _ptr(ns), len(ms), _ptr(C), _ptr(B)),
            "grouped_gemm_blockscaled")
     return C.reshape(shape), B.reshape(shape)
+
+
+def dequant_w_128x128(q, s, lib=None):
+    """FP8 -> BF16 weight conversion with 128x128 block scales: ``w = bf16(fl32(dec(q) * s))``.
+
+    ``q`` uint8 codes ``[N, K]`` (or ``[E, N, K]``), ``s`` fp32 ``[N/128, K/128]`` (``[E, N/128, K/128]``).
+    Returns bf16 bit patterns (uint16) of ``q``'s shape.
+    """
+    lib = lib or load()
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    K = q.shape[-1]
+    N = int(np.prod(q.shape[:-1]))
+    assert s.size == (N // 128) * (K // 128)
+    w = np.empty(q.shape, dtype=np.uint16)
+    _check(lib.oracle_dequant_w_128x128(_ptr(q), _ptr(s), N, K, _ptr(w)), "dequant_w_128x128")
+    return w

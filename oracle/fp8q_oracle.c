@@ -33,6 +33,13 @@
  *    B = sum_k |a_deq[m,k]| * |w_deq[n,k]|.  Promotion of partial sums at every
  *    128-element K interval is how a GPU reaches this value in fp32; the
  *    oracle does not model it, it computes the value itself.
+ *  - FP8 -> BF16 weight conversion (page "deepseek-ai/DeepSeek-V3" on the
+ *    ai.atomgit.com mirror, "How to Run Locally": only FP8 weights are
+ *    published, with a script that converts them to BF16; the CSDN page lists
+ *    an analysis of that conversion).  The pages do not give its arithmetic;
+ *    the reading taken here is the one the GEMM's promotion uses: every code
+ *    times its 128x128 block's scale in fp32, then rounded to bf16 to nearest
+ *    even: w = bf16(fl32(dec(q) * s)).
  *
  * Layouts (a reading; the pages are silent): row-major, K contiguous.
  * Activation scales s_a are stored K-block-major, s_a[kb * M + m]; weight scales
@@ -43,6 +50,9 @@
  * operation written here is one IEEE-754 binary32 operation.
  *
  * Pins: tests/test_oracle_*.py check this file against hand-worked E4M3 cases,
+ * (for the dequantization) exact rational rounding of every code times sampled
+ * scales, the power-of-two and unit-code closed forms, and a per-block scale
+ * pattern,
  * the OCP closed-form code table, a brute-force nearest-value encoder over all
  * bf16 inputs, sign/scale invariants, a lossless special case equal to a
  * float64 numpy matmul, and exact rational sums on tiny shapes.
@@ -189,6 +199,35 @@ int oracle_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, 
         }
     }
     return bad ? -2 : 0;
+}
+
+/* ---- FP8 -> BF16 block dequantization ----------------------------------------
+ * Round a finite fp32 value to the nearest bf16 (ties to even): keep the upper
+ * 16 bits after adding half of the dropped part, with the tie going to the even
+ * upper half. */
+static uint16_t f32_to_bf16(float v) {
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    const uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) return (uint16_t)(upper + 1u);
+    return (uint16_t)upper;
+}
+
+/* w[n][k] = bf16(fl32(dec(q[n][k]) * s[n/128][k/128])).  The product of a code
+ * (at most 4 significant bits) and an fp32 scale (24) is exact in double, so
+ * converting it to float rounds once, as an fp32 multiply would. */
+int oracle_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t K, uint16_t *w) {
+    if (N < 0 || K < 0 || N % GROUP || K % GROUP) return -1;
+    int64_t KB = K / GROUP;
+    for (int64_t i = 0; i < N * K; i++)
+        if ((q[i] & 0x7Fu) == 0x7Fu) return -2; /* NaN code */
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            const double exact = oracle_e4m3_decode(q[n * K + k]) * (double)s[(n / GROUP) * KB + k / GROUP];
+            w[n * K + k] = f32_to_bf16((float)exact);
+        }
+    return 0;
 }
 
 /* ---- block-scaled GEMM ------------------------------------------------------

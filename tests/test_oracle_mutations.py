@@ -9,6 +9,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_dequant as td
 import test_oracle_e4m3 as te
 import test_oracle_gemm as tg
 import test_oracle_quant as tq
@@ -35,6 +36,9 @@ MUTATIONS = {
     "grouped_expert_off_by_one": ("const uint8_t *w_e = qw + e * N * K;",
                                   "const uint8_t *w_e = qw + (e > 0 ? e - 1 : 0) * N * K;"),
     "zero_group_sign_lost": ("return signbit(x) ? 0x80u : 0x00u; /* all-zero group */", "return 0x00u;"),
+    "dequant_truncates_to_bf16": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))", "if (0)"),
+    "dequant_bf16_ties_away": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))", "if (lower >= 0x8000u)"),
+    "dequant_scale_ignores_k_block": ("(double)s[(n / GROUP) * KB + k / GROUP]", "(double)s[(n / GROUP) * KB]"),
 }
 
 
@@ -53,6 +57,10 @@ def pins():
         (tg.test_lossless_case_equals_float64_matmul, {"M": 37, "N": 256, "K": 384}),
         (tg.test_exact_rational_brute_force, {"M": 2, "K": 256}),
         (tg.test_grouped_lossless_and_padding, {}),
+        (td.test_every_code_times_sampled_scales_is_rounded_exactly, {}),
+        (td.test_unit_code_returns_the_scale_and_powers_of_two_are_exact, {}),
+        (td.test_double_rounding_follows_the_fp32_route, {}),
+        (td.test_each_block_uses_its_own_scale, {}),
     ]
     for case in tq.load_golden()["act_groups"]:
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
