@@ -52,7 +52,10 @@ DESCRIPTIONS = {
     "decode": "decode-shaped small M: A bf16 [64,7168], W pre-quantized E4M3 [18432,7168] with 128x128 fp32 "
               "scales; 1x128 act quant + block-scaled FP8 GEMM -> bf16 [64,18432]",
     "tiny": "tiny: A bf16 [128,512] with 4 outlier channels x50, W bf16 [256,512]; full path -> bf16 [128,256]",
+    "dequant": "FP8 -> BF16 weight conversion with 128x128 scales: E4M3 [18432,7168] (uniform finite codes), "
+               "scales [144,56] ~U(1e-4,1e-2) -> bf16 [18432,7168]",
 }
+DEQUANT_METRIC = "FP8 -> BF16 128x128 block dequantization GB/s (% HBM peak)"
 
 
 def log(msg):
@@ -92,6 +95,17 @@ class Workload:
 
         M, N, K = d["M"], d["N"], d["K"]
         self.M, self.N, self.K = M, N, K
+        self.step_count = 0
+        if name == "dequant":
+            self.qw = torch.from_numpy(d["wq"]).to(dev)
+            self.sw = torch.from_numpy(d["sw"]).to(dev)
+            self.w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+            self.flops = 0.0
+            self.bytes = 3 * N * K + 4 * (N // 128) * (K // 128)
+            self.kernels = [("dequant_w_128x128", lambda: fq.fp8q_dequant_w_128x128(self.qw, self.sw, w=self.w),
+                             {"bytes": self.bytes})]
+            torch.cuda.synchronize()
+            return
         self.a = bf16(d["a"])
         self.qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
         self.sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
@@ -153,6 +167,18 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
     d = wk.host
     N, K = wk.N, wk.K
     lib = oracle.load()
+    if wk.name == "dequant":
+        # calibrate on one 128-row block row, then convert about target_s seconds' worth of block rows
+        t0 = time.perf_counter()
+        oracle.dequant_w_128x128(d["wq"][:128], d["sw"][:1], lib=lib)
+        per = time.perf_counter() - t0
+        nb = int(max(1, min(N // 128, target_s / max(per, 1e-6))))
+        t1 = time.perf_counter()
+        oracle.dequant_w_128x128(d["wq"][:128 * nb], d["sw"][:nb], lib=lib)
+        t = time.perf_counter() - t1
+        byts = 3 * 128 * nb * K + 4 * nb * (K // 128)
+        return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+                "sample": f"{128 * nb} of the {N} weight rows (K={K}) converted; {t:.1f} s"}
     if wk.name == "moe":
         e = 0
         off = d["routing"].offsets
@@ -367,7 +393,10 @@ def main():
     gname, _, gwork = wk.kernels[-1]
     g = kernels[gname]
     traffic = profiled_traffic(gname, args.workload)
-    if args.workload == "decode":
+    if args.workload == "dequant":
+        roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
+    elif args.workload == "decode":
         roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
@@ -375,10 +404,11 @@ def main():
                 "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
     roof["algorithmic_bytes"] = int(gwork["bytes"])
 
+    dq = args.workload == "dequant"
     out = {
-        "metric": METRIC,
-        "value": round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
+        "metric": DEQUANT_METRIC if dq else METRIC,
+        "value": round(wk.bytes / (ms_step * 1e-3) / 1e9, 1) if dq else round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "GB/s" if dq else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -387,7 +417,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3 -> bf16" if dq else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,
                    "K": wk.K, "out": "bf16", "parallelism": "single GPU"},

@@ -7,11 +7,13 @@ this package is its Python binding.  Entry points (same names as the C functions
   fp8q_quant_w_128x128(w)                      bf16 [N, K] -> (E4M3 [N, K], fp32 scales [N/128, K/128])
   fp8q_gemm_blockscaled(qa, sa, qw, sw)        -> C = A W^T, bf16 or fp32 [M, N]
   fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets)   MoE experts, one segment of rows each
+  fp8q_dequant_w_128x128(q, s)                 E4M3 [N, K] + fp32 [N/128, K/128] -> bf16 [N, K]
 """
 from ._binding import (  # noqa: F401
     OUT_BF16,
     OUT_F32,
     LIB_PATH,
+    fp8q_dequant_w_128x128,
     fp8q_gemm_blockscaled,
     fp8q_grouped_gemm_blockscaled,
     fp8q_quant_act_1x128,

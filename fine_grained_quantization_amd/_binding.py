@@ -37,8 +37,9 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_quant_w_128x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
+        lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_gemm_blockscaled,
-                  lib.fp8q_grouped_gemm_blockscaled):
+                  lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128):
             f.restype = ctypes.c_int
         lib.fp8q_status_string.argtypes = [I]
         lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -121,6 +122,25 @@ def fp8q_quant_w_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torc
     _check(load_library().fp8q_quant_w_128x128(_ptr(w), rows, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
            "fp8q_quant_w_128x128")
     return q, s
+
+
+def fp8q_dequant_w_128x128(q: torch.Tensor, s: torch.Tensor, w: torch.Tensor | None = None, stream=None):
+    """FP8 -> BF16 weight conversion with 128x128 block scales.  ``q`` E4M3 codes [N, K] (or an expert stack
+    [E, N, K]), ``s`` float32 [N/128, K/128] (``[E, N/128, K/128]``) -> ``w`` bf16 of ``q``'s shape."""
+    _need(q, "q", _FP8, (2, 3))
+    _need(s, "s", (torch.float32,))
+    K = q.shape[-1]
+    rows = q.numel() // K if K else 0
+    if s.numel() != (rows // 128) * (K // 128):
+        raise ValueError("s has the wrong size")
+    if w is None:
+        w = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _need(w, "w", _BF16)
+    if w.numel() != q.numel():
+        raise ValueError("w has the wrong size")
+    _check(load_library().fp8q_dequant_w_128x128(_ptr(q), _ptr(s), rows, K, _ptr(w), _stream_ptr(stream)),
+           "fp8q_dequant_w_128x128")
+    return w
 
 
 def _out_code(out_dtype):

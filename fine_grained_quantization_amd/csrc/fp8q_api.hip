@@ -83,6 +83,17 @@ int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, fl
     return finish(fp8q::launch_quant_w_128x128(w, N, K, q, s, static_cast<hipStream_t>(stream)));
 }
 
+int fp8q_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t K, uint16_t *w, void *stream) {
+    if (N < 0 || K < 0 || N % 128 || K % 128) return FP8Q_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!q || !s || !w) return FP8Q_ERR_NULL;
+    if (!aligned16(q) || !aligned16(s) || !aligned16(w)) return FP8Q_ERR_ALIGN;
+    if (K / 128 > kMaxGrid / N * 8) return FP8Q_ERR_SHAPE;  // N * K / 8192 workgroups
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_dequant_w_128x128(q, s, N, K, w, static_cast<hipStream_t>(stream)));
+}
+
 int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                           int out_dtype, int64_t M, int64_t N, int64_t K, void *stream) {
     if (M < 0 || N < 0 || K < 128 || K > kMaxK || N % 128 || K % 128) return FP8Q_ERR_SHAPE;

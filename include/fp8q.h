@@ -78,6 +78,19 @@ int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, fl
  * Requires N % 128 == 0, K % 128 == 0. */
 int fp8q_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* FP8 -> BF16 weight conversion with 128x128 block scales (page
+ * "deepseek-ai/DeepSeek-V3", "How to Run Locally": the weights are published in
+ * FP8, with a script that converts them to BF16).  The pages do not give the
+ * arithmetic; this library reads it as every code times its block's scale in
+ * fp32, rounded to bf16 to nearest even:
+ *   w[n,k] = bf16(fl32(E4M3(q[n,k]) * s[n/128][k/128]))
+ *   q : E4M3 [N, K]             (input; an expert stack [E][N', K] is passed as N = E * N')
+ *   s : fp32 [N/128][K/128]     (input)
+ *   w : bf16 [N, K]             (output, as uint16_t bit patterns)
+ * Requires N % 128 == 0, K % 128 == 0.  Codes 0x7F / 0xFF (NaN) are outside the
+ * contract (the quantizers never produce them); they convert to NaN. */
+int fp8q_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t K, uint16_t *w, void *stream);
+
 /* Block-scaled FP8 GEMM, the Linear y = x W^T (the passages on FP8 GEMM inputs
  * with BF16/FP32 outputs and on FP32 promotion):
  *   C[m,n] = sum_kb  s_a[kb][m] * s_w[n/128][kb] * (sum_{k in kb} qa[m,k] * qw[n,k])

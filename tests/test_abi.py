@@ -25,10 +25,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(fp8q_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8q_quant_act_1x128", "fp8q_quant_w_128x128", "fp8q_gemm_blockscaled",
-              "fp8q_grouped_gemm_blockscaled", "fp8q_status_string", "fp8q_version"):
+              "fp8q_grouped_gemm_blockscaled", "fp8q_dequant_w_128x128", "fp8q_status_string", "fp8q_version"):
         assert n in names
 
 
@@ -75,6 +75,12 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_gemm_blockscaled(A, A, A, None, B, 1, 4, 128, 128, None) == -1
     assert lib.fp8q_grouped_gemm_blockscaled(A, A, A, A, B, 0, None, 2, 128, 128, 128, None) == -1
     assert lib.fp8q_quant_act_1x128(MIS, 4, 128, B, B, None) == -3
+    # dequantization
+    assert lib.fp8q_dequant_w_128x128(A, B, 100, 128, B, None) == -2
+    assert lib.fp8q_dequant_w_128x128(A, B, 128, 64, B, None) == -2
+    assert lib.fp8q_dequant_w_128x128(None, None, 0, 128, None, None) == 0
+    assert lib.fp8q_dequant_w_128x128(A, None, 128, 128, B, None) == -1
+    assert lib.fp8q_dequant_w_128x128(A, B, 128, 128, MIS, None) == -3
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, MIS, 0, 4, 128, 128, None) == -3
 
 

@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-SEEDS = {"tiny": 0, "up": 1, "down": 2, "moe": 3, "decode": 4}
+SEEDS = {"tiny": 0, "up": 1, "down": 2, "moe": 3, "decode": 4, "dequant": 5}
 
 # tensor ids inside one workload's seed
 T_A, T_W, T_OUTLIER, T_X, T_Y, T_LOGITS, T_WQ, T_SW = 0, 1, 2, 3, 4, 5, 6, 7
@@ -199,4 +199,13 @@ def decode(M=64, N=18432, K=7168):
     return {"name": "decode", "a": a, "wq": wq, "sw": sw, "M": M, "N": N, "K": K}
 
 
-WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode}
+def dequant(N=18432, K=7168):
+    """FP8 weights of the up-projection's shape with 128x128 scales, to be converted to BF16: codes uniform
+    over the 254 finite E4M3 codes, scales ~U(1e-4, 1e-2) (the decode workload's recipe)."""
+    s = SEEDS["dequant"]
+    wq = finite_e4m3_codes(s, T_WQ, (N, K))
+    sw = uniform_f32(s, T_SW, (N // 128, K // 128), 1e-4, 1e-2)
+    return {"name": "dequant", "wq": wq, "sw": sw, "M": 0, "N": N, "K": K}
+
+
+WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant}
