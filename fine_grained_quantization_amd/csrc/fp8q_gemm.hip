@@ -472,6 +472,39 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
     }
 
     // Epilogue: lane holds C[m][n .. n+3] of each subtile; rows outside [m0, mend) are not stored.
+    if constexpr (OUT_BF16) {
+        // Through LDS, so that the stores are row-contiguous: each wave writes its 64 x WN bf16 block into
+        // the (now idle) stages, waves 0-3 into stage0 and 4-7 into stage1, then reads it back 16 bytes per
+        // lane along rows and stores whole row segments.  The 16-byte chunks of row r are rotated by r, which
+        // spreads a column of rows over the banks while every row stays 16-byte aligned.
+        constexpr int CPR = 2 * NSUB;  // 16-byte chunks per row of the block
+        constexpr int RS = CPR * 16;
+        static_assert(4 * 64 * RS <= TileLoader<BN>::kStageBytes, "epilogue staging");
+        __builtin_amdgcn_s_waitcnt(0);  // the last (out-of-range) copies into the stages have retired
+        __syncthreads();                // and every wave is done reading the stages
+        uint8_t *blk = (wave < 4 ? stage0 : stage1) + (wave & 3) * 64 * RS;
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+            for (int ni = 0; ni < NSUB; ni++) {
+                const int r = mi * 16 + (lane & 15);
+                const int ch = ni * 2 + (lane >> 5), half = (lane >> 4) & 1;
+                uint2 o;
+                o.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+                o.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+                *reinterpret_cast<uint2 *>(blk + r * RS + ((ch + r) % CPR) * 16 + half * 8) = o;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPR; j++) {
+            const int idx = j * 64 + lane;
+            const int r = idx / CPR, ch = idx % CPR;
+            const int64_t m = m0 + wm * 64 + r, n = nw0 + ch * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(blk + r * RS + ((ch + r) % CPR) * 16);
+            if (m < mend && n < N) *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(c) + m * N + n) = v;
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; mi++) {
         const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
