@@ -271,6 +271,10 @@ class _Rec:
 
 
 GEMM_SOURCES = ("fine_grained_quantization_amd/csrc/fp8q_gemm.hip", "fine_grained_quantization_amd/csrc/fp8q_device.h")
+QUANT_SOURCES = ("fine_grained_quantization_amd/csrc/fp8q_quant.hip", "fine_grained_quantization_amd/csrc/fp8q_device.h")
+# The sources each reported kernel is built from (its recorded traffic is stale once they change).
+KERNEL_SOURCES = {"gemm_blockscaled": GEMM_SOURCES, "grouped_gemm_blockscaled": GEMM_SOURCES,
+                  "dequant_w_128x128": QUANT_SOURCES}
 
 
 def sources_sha256(paths=GEMM_SOURCES):
@@ -295,7 +299,8 @@ def profiled_traffic(kname, workload):
             if ":" in line and line.strip().startswith(("source_sha256", "traffic_bytes_per_launch")):
                 k, v = line.strip().strip("`").split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_sha256") != sources_sha256() or "traffic_bytes_per_launch" not in fields:
+    srcs = KERNEL_SOURCES.get(kname, GEMM_SOURCES)
+    if fields.get("source_sha256") != sources_sha256(srcs) or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
