@@ -71,6 +71,10 @@ def load(path: str | None = None):
         lib.oracle_grouped_gemm_blockscaled.restype = ctypes.c_int
         lib.oracle_dequant_w_128x128.argtypes = [P, P, I64, I64, P]
         lib.oracle_dequant_w_128x128.restype = ctypes.c_int
+        lib.oracle_moe_route_topk.argtypes = [P, I64, I64, I64, I64, P, P, P, P, I64]
+        lib.oracle_moe_route_topk.restype = ctypes.c_int
+        lib.oracle_moe_gather_fp8.argtypes = [P, P, I64, I64, P, I64, P, P]
+        lib.oracle_moe_gather_fp8.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -94,6 +98,8 @@ def _check(rc: int, what: str):
         raise ValueError(f"{what}: bad shape or index")
     if rc == -2:
         raise ValueError(f"{what}: non-finite input (finite input is a precondition)")
+    if rc == -3:
+        raise ValueError(f"{what}: the output has fewer rows than the layout needs")
     if rc != 0:
         raise RuntimeError(f"{what}: status {rc}")
 
@@ -234,3 +240,70 @@ def dequant_w_128x128(q, s, lib=None):
     w = np.empty(q.shape, dtype=np.uint16)
     _check(lib.oracle_dequant_w_128x128(_ptr(q), _ptr(s), N, K, _ptr(w)), "dequant_w_128x128")
     return w
+
+
+# ---------------------------------------------------------------------------
+# MoE routing and the FP8 row gather
+# ---------------------------------------------------------------------------
+
+class Routing:
+    """Result of :func:`moe_route_topk`.
+
+    ``topk_idx`` int32 ``[T, k]``: token t's experts by decreasing logit (ties: lower index first).
+    ``offsets`` int32 ``[E+1]``: expert e owns rows ``offsets[e] .. offsets[e+1]`` (multiples of ``pad``).
+    ``row_of`` int32 ``[T, k]``: the row carrying token t's j-th expert.
+    ``row_token`` int32 ``[rows]``: the token a row carries, -1 for empty rows and rows past ``offsets[E]``.
+    """
+
+    def __init__(self, topk_idx, offsets, row_of, row_token):
+        self.topk_idx, self.offsets, self.row_of, self.row_token = topk_idx, offsets, row_of, row_token
+
+    @property
+    def counts(self):
+        return np.bincount(self.topk_idx.ravel(), minlength=len(self.offsets) - 1).astype(np.int64)
+
+    @property
+    def M(self):
+        """Rows of the layout (``offsets[E]``)."""
+        return int(self.offsets[-1])
+
+
+def moe_route_capacity(T: int, E: int, k: int, pad: int = 128) -> int:
+    """Rows enough for any routing of T tokens to k of E experts: T*k plus pad-1 per expert, rounded up
+    to a multiple of pad."""
+    return ((T * k + E * (pad - 1)) + pad - 1) // pad * pad
+
+
+def moe_route_topk(logits, k: int, pad: int = 128, rows: int | None = None, lib=None) -> Routing:
+    """Top-k gating and the expert-sorted layout (readings in ``fp8q_oracle.c``).  ``logits`` fp32
+    ``[T, E]``; ``rows`` is the length of ``row_token`` (default: exactly ``offsets[E]``)."""
+    lib = lib or load()
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    cap = moe_route_capacity(T, E, k, pad) if rows is None else rows
+    topk_idx = np.empty((T, k), dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    row_of = np.empty((T, k), dtype=np.int32)
+    row_token = np.empty(cap, dtype=np.int32)
+    _check(lib.oracle_moe_route_topk(_ptr(logits), T, E, k, pad, _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
+                                     _ptr(row_token), cap), "moe_route_topk")
+    if rows is None:
+        row_token = row_token[: int(offsets[-1])].copy()
+    return Routing(topk_idx, offsets, row_of, row_token)
+
+
+def moe_gather_fp8(q, s, row_token, lib=None):
+    """Expert-sorted FP8 rows: ``qa[r] = q[row_token[r]]`` and ``sa[:, r] = s[:, row_token[r]]``, zero codes
+    and scale 0 where ``row_token[r] == -1``.  ``q`` uint8 ``[T, K]``, ``s`` fp32 ``[K/128, T]``.
+    Returns ``(qa [rows, K], sa [K/128, rows])``."""
+    lib = lib or load()
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    row_token = _c(row_token, np.int32)
+    T, K = q.shape
+    rows = len(row_token)
+    qa = np.empty((rows, K), dtype=np.uint8)
+    sa = np.empty((K // 128, rows), dtype=np.float32)
+    _check(lib.oracle_moe_gather_fp8(_ptr(q), _ptr(s), T, K, _ptr(row_token), rows, _ptr(qa), _ptr(sa)),
+           "moe_gather_fp8")
+    return qa, sa

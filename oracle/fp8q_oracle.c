@@ -40,6 +40,12 @@
  *    the reading taken here is the one the GEMM's promotion uses: every code
  *    times its 128x128 block's scale in fp32, then rounded to bf16 to nearest
  *    even: w = bf16(fl32(dec(q) * s)).
+ *  - MoE routing and the FP8 row gather (page "DeepSeek starts updating
+ *    frequently", the list of TileKernels features: top-k gating and the
+ *    token-to-expert mapping): top-k experts per token by logit, and the
+ *    expert-sorted, 128-padded layout of the quantized rows that the grouped
+ *    GEMM consumes.  The readings (tie rule, segment order, empty rows) are
+ *    stated beside the functions at the end of this file.
  *
  * Layouts (a reading; the pages are silent): row-major, K contiguous.
  * Activation scales s_a are stored K-block-major, s_a[kb * M + m]; weight scales
@@ -52,7 +58,10 @@
  * Pins: tests/test_oracle_*.py check this file against hand-worked E4M3 cases,
  * (for the dequantization) exact rational rounding of every code times sampled
  * scales, the power-of-two and unit-code closed forms, and a per-block scale
- * pattern,
+ * pattern, (for routing) a pairwise check of the top-k definition on random
+ * and tie-heavy logits, library special cases (k = 1 is argmax, k = E a stable
+ * sort), a hand-worked layout and the layout invariants, (for the gather)
+ * numpy indexing and its commutation with the row-wise quantizer,
  * the OCP closed-form code table, a brute-force nearest-value encoder over all
  * bf16 inputs, sign/scale invariants, a lossless special case equal to a
  * float64 numpy matmul, and exact rational sums on tiny shapes.
@@ -285,6 +294,90 @@ int oracle_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const ui
         const uint8_t *w_e = qw + e * N * K;
         const float *s_e = sw + e * NB * KB;
         C[i] = dot_dequant(qa + m * K, sa, M_total, m, w_e + n * K, s_e + (n / GROUP) * KB, K, &B[i]);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * MoE routing and the FP8 row gather (page "DeepSeek starts updating
+ * frequently" on deepinsightai.io, the list of TileKernels features: a gating
+ * step selects each token's top-k experts, and a routing step maps tokens to
+ * experts; the same page's DeepEP V2 test uses 8K tokens, hidden 7168, the top
+ * 8 experts and FP8 dispatch).  The pages fix neither the tie rule nor the
+ * expert-sorted layout.  Readings taken here:
+ *  - token t selects the k experts with the largest logits, listed by
+ *    decreasing logit; of two equal logits (numerically: -0 equals +0) the
+ *    lower expert index comes first;
+ *  - expert e owns one segment of rows holding its tokens in ascending token
+ *    order, padded with empty rows to a multiple of `pad` (128: the 128-row
+ *    granularity of the grouped GEMM's scales and tiles); the segments follow
+ *    each other in expert order from row 0;
+ *  - an empty row carries all-zero codes and scale 0.
+ * ------------------------------------------------------------------------- */
+
+/* logits fp32 [T][E] (finite).  Outputs: topk_idx int32 [T][k]; offsets int32
+ * [E+1] (segment e is rows [offsets[e], offsets[e+1])); row_of int32 [T][k]
+ * (the row that carries token t's j-th expert); row_token int32 [rows] (the
+ * token a row carries, -1 for empty rows and for rows past offsets[E]).
+ * Returns 0, -1 for bad sizes, -2 for a non-finite logit, -3 when `rows` is
+ * smaller than the layout. */
+int oracle_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t k, int64_t pad, int32_t *topk_idx,
+                          int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows) {
+    if (T < 0 || E < 1 || E > 4096 || k < 1 || k > E || pad < 1 || rows < 0) return -1;
+    for (int64_t i = 0; i < T * E; i++)
+        if (!isfinite(logits[i])) return -2;
+    unsigned char chosen[E];
+    for (int64_t t = 0; t < T; t++) {
+        const float *v = logits + t * E;
+        memset(chosen, 0, sizeof chosen);
+        for (int64_t j = 0; j < k; j++) {
+            /* the largest logit not chosen yet; scanning upwards with a strict
+             * comparison keeps the lower index among equal logits */
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++)
+                if (!chosen[e] && (best < 0 || v[e] > v[best])) best = e;
+            chosen[best] = 1;
+            topk_idx[t * k + j] = (int32_t)best;
+        }
+    }
+    int64_t count[E];
+    for (int64_t e = 0; e < E; e++) count[e] = 0;
+    for (int64_t i = 0; i < T * k; i++) count[topk_idx[i]]++;
+    offsets[0] = 0;
+    int64_t end = 0;
+    for (int64_t e = 0; e < E; e++) {
+        end += (count[e] + pad - 1) / pad * pad;
+        if (end > INT32_MAX) return -1;
+        offsets[e + 1] = (int32_t)end;
+    }
+    if (rows < end) return -3;
+    for (int64_t r = 0; r < rows; r++) row_token[r] = -1;
+    int64_t next[E];
+    for (int64_t e = 0; e < E; e++) next[e] = offsets[e];
+    for (int64_t t = 0; t < T; t++) /* ascending tokens: each segment fills in token order */
+        for (int64_t j = 0; j < k; j++) {
+            int64_t e = topk_idx[t * k + j];
+            int64_t r = next[e]++;
+            row_of[t * k + j] = (int32_t)r;
+            row_token[r] = (int32_t)t;
+        }
+    return 0;
+}
+
+/* Expert-sorted FP8 activations: row r of qa (and of the scales sa, K-block-major
+ * [K/128][rows]) is token row_token[r]'s row of q / s (s: [K/128][T]), or
+ * all-zero codes with scale 0 when row_token[r] is -1.  Returns -1 for bad
+ * sizes or a token index outside [-1, T). */
+int oracle_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K, const int32_t *row_token,
+                          int64_t rows, uint8_t *qa, float *sa) {
+    if (T < 0 || K < 0 || K % GROUP || rows < 0) return -1;
+    for (int64_t r = 0; r < rows; r++)
+        if (row_token[r] < -1 || row_token[r] >= T) return -1;
+    int64_t KB = K / GROUP;
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t t = row_token[r];
+        for (int64_t k = 0; k < K; k++) qa[r * K + k] = t >= 0 ? q[t * K + k] : 0;
+        for (int64_t kb = 0; kb < KB; kb++) sa[kb * rows + r] = t >= 0 ? s[kb * T + t] : 0.0f;
     }
     return 0;
 }

@@ -1,7 +1,7 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU; the real oracle is not
-touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm against it.  At least one
+touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe against it.  At least one
 pin must fail for every planted mistake.
 """
 import os
@@ -12,6 +12,7 @@ import oracle
 import test_oracle_dequant as td
 import test_oracle_e4m3 as te
 import test_oracle_gemm as tg
+import test_oracle_moe as tm
 import test_oracle_quant as tq
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "fp8q_oracle.c")).read()
@@ -39,6 +40,14 @@ MUTATIONS = {
     "dequant_truncates_to_bf16": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))", "if (0)"),
     "dequant_bf16_ties_away": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))", "if (lower >= 0x8000u)"),
     "dequant_scale_ignores_k_block": ("(double)s[(n / GROUP) * KB + k / GROUP]", "(double)s[(n / GROUP) * KB]"),
+    "route_ties_to_higher_index": ("(best < 0 || v[e] > v[best])", "(best < 0 || v[e] >= v[best])"),
+    "route_segments_descending": ("for (int64_t t = 0; t < T; t++) /* ascending tokens",
+                                  "for (int64_t t = T - 1; t >= 0; t--) /* ascending tokens"),
+    "route_no_padding": ("end += (count[e] + pad - 1) / pad * pad;", "end += count[e];"),
+    "route_signed_zero_ordered": ("(best < 0 || v[e] > v[best])",
+                                  "(best < 0 || v[e] > v[best] || (v[e] == v[best] && signbit(v[best]) && !signbit(v[e])))"),
+    "gather_scale_row_major": ("sa[kb * rows + r] = t >= 0", "sa[r * KB + kb] = t >= 0"),
+    "gather_empty_row_copies_token_0": ("qa[r * K + k] = t >= 0 ? q[t * K + k] : 0;", "qa[r * K + k] = q[(t >= 0 ? t : 0) * K + k];"),
 }
 
 
@@ -61,6 +70,15 @@ def pins():
         (td.test_unit_code_returns_the_scale_and_powers_of_two_are_exact, {}),
         (td.test_double_rounding_follows_the_fp32_route, {}),
         (td.test_each_block_uses_its_own_scale, {}),
+    ]
+    out += [
+        (tm.test_hand_worked_routing, {}),
+        (tm.test_topk_satisfies_the_pairwise_definition, {"T": 25, "E": 64, "k": 8, "heavy": True}),
+        (tm.test_k1_is_argmax_and_k_equal_E_is_a_stable_sort, {}),
+        (tm.test_layout_invariants, {"T": 300, "E": 64, "k": 8, "extra": 200}),
+        (tm.test_gather_hand_case, {}),
+        (tm.test_gather_matches_numpy_indexing, {}),
+        (tm.test_gather_commutes_with_the_row_quantizer, {}),
     ]
     for case in tq.load_golden()["act_groups"]:
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
