@@ -46,9 +46,9 @@ DESCRIPTIONS = {
           "[4096,18432]",
     "down": "dense FFN down-projection: A = bf16(SiLU(x)*y) [4096,18432], W bf16 [7168,18432] ~N(0,0.02); "
             "1x128 act quant + 128x128 weight quant + block-scaled FP8 GEMM -> bf16 [4096,7168]",
-    "moe": "MoE layer: 8192 tokens x 7168, top-8 of 64 experts (segments padded to 128 rows), expert W bf16 "
-           "[64][2048,7168]; 1x128 act quant of the padded rows + 128x128 weight quant + grouped block-scaled "
-           "FP8 GEMM -> bf16",
+    "moe": "MoE layer: 8192 tokens x 7168 bf16 ~N(0,1), router logits [8192,64] ~N(0,1), expert W bf16 "
+           "[64][2048,7168] ~N(0,0.02); 1x128 act quant of the tokens + top-8 routing + FP8 row gather into "
+           "128-padded expert segments + 128x128 weight quant + grouped block-scaled FP8 GEMM -> bf16",
     "decode": "decode-shaped small M: A bf16 [64,7168], W pre-quantized E4M3 [18432,7168] with 128x128 fp32 "
               "scales; 1x128 act quant + block-scaled FP8 GEMM -> bf16 [64,18432]",
     "tiny": "tiny: A bf16 [128,512] with 4 outlier channels x50, W bf16 [256,512]; full path -> bf16 [128,256]",
@@ -106,6 +106,9 @@ class Workload:
                              {"bytes": self.bytes})]
             torch.cuda.synchronize()
             return
+        if name == "moe":
+            self._init_moe(d, bf16, dev)
+            return
         self.a = bf16(d["a"])
         self.qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
         self.sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
@@ -125,24 +128,65 @@ class Workload:
             kernels.append(("quant_w_128x128", lambda: fq.fp8q_quant_w_128x128(self.w, self.qw, self.sw),
                             {"bytes": w_bytes(wrows, K)}))
         self.c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        if name == "moe":
-            r = d["routing"]
-            self.off = torch.from_numpy(r.offsets).to(dev)
-            E = d["E"]
-            real_rows = int(r.counts.sum())
-            self.flops = 2.0 * real_rows * N * K       # padding rows are not counted as work
-            gb = M * K + E * N * K + 4 * M * (K // 128) + 4 * E * (N // 128) * (K // 128) + 2 * M * N
-            kernels.append(("grouped_gemm_blockscaled",
-                            lambda: fq.fp8q_grouped_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, self.off,
-                                                                     c=self.c),
-                            {"flops": self.flops, "bytes": gb}))
-        else:
-            self.flops = 2.0 * M * N * K
-            kernels.append(("gemm_blockscaled",
-                            lambda: fq.fp8q_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, c=self.c),
-                            {"flops": self.flops, "bytes": gemm_bytes(M, N, K)}))
+        self.flops = 2.0 * M * N * K
+        kernels.append(("gemm_blockscaled",
+                        lambda: fq.fp8q_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, c=self.c),
+                        {"flops": self.flops, "bytes": gemm_bytes(M, N, K)}))
         self.step_count = 0
         self.kernels = kernels
+        torch.cuda.synchronize()
+
+    def _init_moe(self, d, bf16, dev):
+        """Tokens are quantized once, routed on the GPU, and their FP8 rows gathered into the expert-sorted,
+        128-padded layout that the grouped GEMM reads (sized to the routing capacity, so nothing is read back
+        to the host inside a step)."""
+        import torch
+
+        import fine_grained_quantization_amd as fq
+
+        T, E, k, N, K = d["T"], d["E"], d["topk"], d["N"], d["K"]
+        rows = fq.fp8q_moe_route_capacity(T, E, k)
+        self.M = rows
+        self.tokens = bf16(d["tokens"])
+        self.logits = torch.from_numpy(d["logits"]).to(dev)
+        self.qt = torch.empty((T, K), dtype=torch.uint8, device=dev)
+        self.st = torch.empty((K // 128, T), dtype=torch.float32, device=dev)
+        self.route_out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+                          torch.empty(E + 1, dtype=torch.int32, device=dev),
+                          torch.empty((T, k), dtype=torch.int32, device=dev),
+                          torch.empty(rows, dtype=torch.int32, device=dev))
+        self.route_ws = torch.empty(fq.load_library().fp8q_moe_route_workspace_bytes(T, E), dtype=torch.uint8,
+                                    device=dev)
+        self.qa = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        self.sa = torch.empty((K // 128, rows), dtype=torch.float32, device=dev)
+        self.w = bf16(d["w"])
+        self.qw = torch.empty(d["w"].shape, dtype=torch.uint8, device=dev)
+        self.sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        self.c = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+        # rows in use (for the byte counts only): one routing outside the timed region
+        fq.fp8q_moe_route_topk(self.logits, k, workspace=self.route_ws, out=self.route_out)
+        used = int(self.route_out[1][-1].item())
+        self.rows_used = used
+        off = self.route_out[1]
+        self.flops = 2.0 * T * k * N * K       # routed (token, expert) rows only; padding rows are not work
+        KB = K // 128
+        route_bytes = 4 * T * E + 4 * 3 * T * k + 4 * rows + 4 * (E + 1)
+        gather_bytes = T * K + 4 * KB * T + used * K + 4 * KB * used + 4 * used
+        gb = used * K + E * N * K + 4 * used * KB + 4 * E * (N // 128) * KB + 2 * used * N
+        self.kernels = [
+            ("quant_act_1x128", lambda: fq.fp8q_quant_act_1x128(self.tokens, self.qt, self.st),
+             {"bytes": act_bytes(T, K)}),
+            ("moe_route_topk", lambda: fq.fp8q_moe_route_topk(self.logits, k, workspace=self.route_ws,
+                                                              out=self.route_out), {"bytes": route_bytes}),
+            ("moe_gather_fp8", lambda: fq.fp8q_moe_gather_fp8(self.qt, self.st, self.route_out[2], self.route_out[3],
+                                                              off, self.qa, self.sa), {"bytes": gather_bytes}),
+            ("quant_w_128x128", lambda: fq.fp8q_quant_w_128x128(self.w, self.qw, self.sw),
+             {"bytes": w_bytes(E * N, K)}),
+            ("grouped_gemm_blockscaled",
+             lambda: fq.fp8q_grouped_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, off, c=self.c),
+             {"flops": self.flops, "bytes": gb}),
+        ]
+        self.step_count = 0
         torch.cuda.synchronize()
 
     def step(self, events=None):
@@ -180,10 +224,10 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
         return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
                 "sample": f"{128 * nb} of the {N} weight rows (K={K}) converted; {t:.1f} s"}
     if wk.name == "moe":
-        e = 0
-        off = d["routing"].offsets
-        lo, hi = int(off[e]), int(off[e + 1])
-        w_bits, a_src = d["w"][e], d["a"][lo:hi]
+        e = 0   # expert 0's routed tokens against its weight (routing by the oracle)
+        r = oracle.moe_route_topk(d["logits"], d["topk"], lib=lib)
+        seg = r.row_token[r.offsets[e]:r.offsets[e + 1]]
+        w_bits, a_src = d["w"][e], d["tokens"][seg[seg >= 0]]
     elif wk.name == "decode":
         w_bits, a_src = None, d["a"]
     else:
@@ -430,6 +474,8 @@ def main():
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }
+    if args.workload == "moe":
+        out["config"]["rows_used"] = wk.rows_used   # M is the routing capacity the buffers are sized to
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wk)

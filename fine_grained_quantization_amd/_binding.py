@@ -38,9 +38,16 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
+        lib.fp8q_moe_route_topk.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, P]
+        lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_gemm_blockscaled,
-                  lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128):
+                  lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
+                  lib.fp8q_moe_gather_fp8):
             f.restype = ctypes.c_int
+        lib.fp8q_moe_route_capacity.argtypes = [I64, I64, I64]
+        lib.fp8q_moe_route_capacity.restype = I64
+        lib.fp8q_moe_route_workspace_bytes.argtypes = [I64, I64]
+        lib.fp8q_moe_route_workspace_bytes.restype = I64
         lib.fp8q_status_string.argtypes = [I]
         lib.fp8q_status_string.restype = ctypes.c_char_p
         lib.fp8q_version.argtypes = []
@@ -196,3 +203,78 @@ def fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets, out_dtype=torch.bfloa
                                                         _ptr(offsets), E, M, N, K, _stream_ptr(stream)),
            "fp8q_grouped_gemm_blockscaled")
     return c
+
+
+def fp8q_moe_route_capacity(T: int, E: int, k: int) -> int:
+    """Rows any routing of T tokens to k of E experts fits in (T*k + 127*E, rounded up to 128)."""
+    n = load_library().fp8q_moe_route_capacity(T, E, k)
+    if n < 0:
+        raise ValueError(f"invalid routing sizes T={T} E={E} k={k}")
+    return n
+
+
+def fp8q_moe_route_topk(logits, k: int, rows: int | None = None, workspace=None, out=None, stream=None):
+    """Top-k gating and the expert-sorted, 128-padded layout.  ``logits`` float32 [T, E] ->
+    ``(topk_idx int32 [T, k], offsets int32 [E+1], row_of int32 [T, k], row_token int32 [rows])``.
+    ``rows`` defaults to :func:`fp8q_moe_route_capacity`; ``workspace`` (any device tensor of at least
+    ``fp8q_moe_route_workspace_bytes(T, E)`` bytes) and ``out`` (the four outputs) are allocated when
+    not given."""
+    _need(logits, "logits", (torch.float32,), 2)
+    T, E = logits.shape
+    lib = load_library()
+    cap = fp8q_moe_route_capacity(T, E, k)
+    rows = cap if rows is None else rows
+    wbytes = lib.fp8q_moe_route_workspace_bytes(T, E)
+    if wbytes < 0:
+        raise ValueError(f"invalid routing sizes T={T} E={E}")
+    if workspace is None:
+        workspace = torch.empty(max(wbytes, 4), dtype=torch.uint8, device=logits.device)
+    if out is None:
+        dev = logits.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty(rows, dtype=torch.int32, device=dev))
+    topk_idx, offsets, row_of, row_token = out
+    for t, n, size in ((topk_idx, "topk_idx", T * k), (offsets, "offsets", E + 1), (row_of, "row_of", T * k),
+                       (row_token, "row_token", rows)):
+        _need(t, n, (torch.int32,))
+        if t.numel() != size:
+            raise ValueError(f"{n} has {t.numel()} elements; expected {size}")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    _check(lib.fp8q_moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
+                                   _ptr(row_token), rows, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "fp8q_moe_route_topk")
+    return topk_idx, offsets, row_of, row_token
+
+
+def fp8q_moe_gather_fp8(q, s, row_of, row_token, offsets, qa=None, sa=None, stream=None):
+    """Expert-sorted FP8 rows for the grouped GEMM.  ``q`` E4M3 [T, K] and ``s`` float32 [K/128, T] (the
+    quantized tokens), ``row_of`` int32 [T, k], ``row_token`` int32 [rows] and ``offsets`` int32 [E+1] (one
+    :func:`fp8q_moe_route_topk` call) -> ``(qa uint8 [rows, K], sa float32 [K/128, rows])``; rows from
+    ``offsets[E]`` on are left as they were."""
+    _need(q, "q", _FP8, 2)
+    _need(s, "s", (torch.float32,))
+    _need(row_of, "row_of", (torch.int32,), 2)
+    _need(row_token, "row_token", (torch.int32,), 1)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    T, K = q.shape
+    if row_of.shape[0] != T:
+        raise ValueError("row_of must have one row per token")
+    k = row_of.shape[1]
+    rows = row_token.numel()
+    E = offsets.numel() - 1
+    if s.numel() != (K // 128) * T:
+        raise ValueError("s has the wrong size")
+    if qa is None:
+        qa = torch.empty((rows, K), dtype=torch.uint8, device=q.device)
+    if sa is None:
+        sa = torch.empty((K // 128, rows), dtype=torch.float32, device=q.device)
+    _need(qa, "qa", _FP8)
+    _need(sa, "sa", (torch.float32,))
+    if qa.numel() != rows * K or sa.numel() != (K // 128) * rows:
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_moe_gather_fp8(_ptr(q), _ptr(s), T, K, k, _ptr(row_of), _ptr(row_token),
+                                              _ptr(offsets), E, rows, _ptr(qa), _ptr(sa), _stream_ptr(stream)),
+           "fp8q_moe_gather_fp8")
+    return qa, sa

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["fp8q_api.hip", "fp8q_quant.hip", "fp8q_gemm.hip"]
+SOURCES = ["fp8q_api.hip", "fp8q_quant.hip", "fp8q_gemm.hip", "fp8q_moe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

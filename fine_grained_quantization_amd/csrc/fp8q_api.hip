@@ -35,6 +35,7 @@ int check_device() {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // 1-D grids: workgroup count must fit in 31 bits
 constexpr int64_t kMaxK = int64_t(1) << 23;  // GEMM tiles address 256 rows of K bytes with 32-bit offsets
@@ -57,6 +58,7 @@ const char *fp8q_status_string(int status) {
         case FP8Q_ERR_NO_DEVICE: return "FP8Q_ERR_NO_DEVICE: no HIP device available";
         case FP8Q_ERR_UNSUPPORTED_DEVICE: return "FP8Q_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950 (MI355X)";
         case FP8Q_ERR_HIP: return "FP8Q_ERR_HIP: the HIP runtime reported a launch error";
+        case FP8Q_ERR_WORKSPACE: return "FP8Q_ERR_WORKSPACE: the workspace is smaller than the call needs";
         default: return "fp8q: unknown status";
     }
 }
@@ -124,6 +126,51 @@ int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint
     if (rc) return rc;
     return finish(fp8q::launch_grouped_gemm_blockscaled(qa, sa, qw, sw, c, out_dtype == FP8Q_OUT_BF16, off, E,
                                                         M_total, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int64_t fp8q_moe_route_capacity(int64_t T, int64_t E, int64_t k) {
+    if (T < 0 || E < 1 || E > fp8q::kMoeMaxExperts || k < 1 || k > E || k > fp8q::kMoeMaxK) return -1;
+    if (T > (int64_t(1) << 40)) return -1;
+    return (T * k + 127 * E + 127) / 128 * 128;
+}
+
+int64_t fp8q_moe_route_workspace_bytes(int64_t T, int64_t E) {
+    if (T < 0 || E < 1 || E > fp8q::kMoeMaxExperts || T > (int64_t(1) << 40)) return -1;
+    return fp8q::moe_route_workspace_bytes(T, E);
+}
+
+int fp8q_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_idx, int32_t *offsets,
+                        int32_t *row_of, int32_t *row_token, int64_t rows, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
+    const int64_t cap = fp8q_moe_route_capacity(T, E, k);
+    if (cap < 0 || rows < cap || rows > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;
+    if (!offsets || !row_token) return FP8Q_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !row_of || !workspace)) return FP8Q_ERR_NULL;
+    if (!aligned4(offsets) || !aligned4(row_token) || (T > 0 && (!aligned4(logits) || !aligned4(topk_idx) ||
+                                                                 !aligned4(row_of) || !aligned4(workspace))))
+        return FP8Q_ERR_ALIGN;
+    if (workspace_bytes < fp8q::moe_route_workspace_bytes(T, E)) return FP8Q_ERR_WORKSPACE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_moe_route_topk(logits, T, (int)E, (int)k, topk_idx, offsets, row_of, row_token, rows,
+                                              static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K, int64_t k, const int32_t *row_of,
+                        const int32_t *row_token, const int32_t *offsets, int64_t E, int64_t rows, uint8_t *qa,
+                        float *sa, void *stream) {
+    if (T < 0 || T > 0x7FFFFFFF || K < 0 || K % 128 || k < 1 || k > 0x7FFFFFFF / (T > 0 ? T : 1) || E < 1 ||
+        E > 0x7FFFFFFF || rows < 0 || rows > 0x7FFFFFFF)
+        return FP8Q_ERR_SHAPE;
+    if (rows == 0 || K == 0) return FP8Q_OK;
+    if (!row_token || !offsets || !qa || !sa || (T > 0 && (!q || !s || !row_of))) return FP8Q_ERR_NULL;
+    if (!aligned16(qa) || !aligned4(sa) || !aligned4(row_token) || !aligned4(offsets) ||
+        (T > 0 && (!aligned16(q) || !aligned4(s) || !aligned4(row_of))))
+        return FP8Q_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_moe_gather_fp8(q, s, T, K, (int)k, row_of, row_token, offsets, (int)E, rows, qa, sa,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -16,6 +16,16 @@ hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uin
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
                                            void *c, bool out_bf16, const int32_t *off, int64_t E, int64_t M_total,
                                            int64_t N, int64_t K, hipStream_t stream);
+// MoE routing: experts at most kMoeMaxExperts, k at most kMoeMaxK.
+constexpr int kMoeMaxExperts = 1024;
+constexpr int kMoeMaxK = 16;
+int64_t moe_route_workspace_bytes(int64_t T, int64_t E);
+hipError_t launch_moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
+                                 int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows,
+                                 int32_t *workspace, hipStream_t stream);
+hipError_t launch_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K, int k,
+                                 const int32_t *row_of, const int32_t *row_token, const int32_t *offsets, int E,
+                                 int64_t rows, uint8_t *qa, float *sa, hipStream_t stream);
 // Number of workgroups the dense GEMM launches for an M x N output (for grid-size validation).
 int64_t gemm_blocks(int64_t M, int64_t N);
 

@@ -56,7 +56,8 @@ typedef enum {
     FP8Q_ERR_DTYPE = -4,              /* unknown output dtype */
     FP8Q_ERR_NO_DEVICE = -5,          /* no HIP device is available */
     FP8Q_ERR_UNSUPPORTED_DEVICE = -6, /* the current device is not gfx950 */
-    FP8Q_ERR_HIP = -7                 /* the HIP runtime reported an error at launch */
+    FP8Q_ERR_HIP = -7,                /* the HIP runtime reported an error at launch */
+    FP8Q_ERR_WORKSPACE = -8           /* the workspace is smaller than the call needs */
 } fp8q_status;
 
 typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 } fp8q_out_dtype;
@@ -107,10 +108,12 @@ int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw,
  *   rows [off[e], off[e+1]) of A are multiplied by expert e's weight.
  *   qa  : E4M3 [M_total, K],      sa : fp32 [K/128][M_total]
  *   qw  : E4M3 [E][N][K],         sw : fp32 [E][N/128][K/128]
- *   off : DEVICE int32 [E+1], non-decreasing, off[0] = 0, off[E] = M_total,
+ *   off : DEVICE int32 [E+1], non-decreasing, off[0] = 0, off[E] <= M_total,
  *         every off[e] a multiple of 128 (segments padded to 128 rows; empty
  *         experts allowed).  Padding rows should carry codes 0 and scale 0 and
- *         then produce exact zeros.
+ *         then produce exact zeros.  Rows [off[E], M_total) are not written, so
+ *         M_total may be the capacity of a routing layout
+ *         (fp8q_moe_route_capacity) without reading off[E] back to the host.
  *   c   : [M_total, N] bf16 or fp32.
  * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23.
  * The offsets live on the device and are not checked on the host.  When they
@@ -126,6 +129,70 @@ const char *fp8q_status_string(int status);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int fp8q_version(void);
+
+/* ---------------------------------------------------------------------------
+ * MoE routing and the FP8 row gather that feed the grouped GEMM (page "DeepSeek
+ * starts updating frequently", deepinsightai.io, the list of TileKernels
+ * features: a gating step selects each token's top-k experts and a routing
+ * step maps tokens to experts; the same page's DeepEP V2 test dispatches 8K
+ * tokens of hidden size 7168 to their top 8 experts in FP8).  The pages fix
+ * neither the tie rule nor the layout; this library takes:
+ *   - token t selects the k experts with the largest logits, listed by
+ *     decreasing logit; between equal logits (-0 equals +0) the lower expert
+ *     index comes first;
+ *   - expert e owns rows [offsets[e], offsets[e+1]), its tokens in ascending
+ *     order followed by empty rows up to a multiple of 128; segments follow
+ *     each other in expert order from row 0;
+ *   - an empty row carries codes 0 and scale 0 (the grouped GEMM then writes
+ *     exact zeros for it).
+ * ------------------------------------------------------------------------- */
+
+/* Rows that any routing of T tokens to k of E experts fits in: T*k + 127*E,
+ * rounded up to a multiple of 128.  Returns -1 for invalid sizes. */
+int64_t fp8q_moe_route_capacity(int64_t T, int64_t E, int64_t k);
+
+/* Bytes of device workspace fp8q_moe_route_topk needs: 4 * E * ceil(T / 64).
+ * Returns -1 for invalid sizes. */
+int64_t fp8q_moe_route_workspace_bytes(int64_t T, int64_t E);
+
+/* Top-k gating and the expert-sorted layout, on the device:
+ *   logits    : fp32 [T][E] (input, finite; NaN gives unspecified experts)
+ *   topk_idx  : int32 [T][k] (output) token t's experts, best first
+ *   offsets   : int32 [E+1] (output) segment starts, offsets[E] = rows in use
+ *   row_of    : int32 [T][k] (output) the row that carries (t, topk_idx[t][j])
+ *   row_token : int32 [rows] (output) the token of each row, -1 for empty rows
+ *               and for every row from offsets[E] on
+ *   rows      : length of row_token; must be >= fp8q_moe_route_capacity(T,E,k)
+ *   workspace : device memory of workspace_bytes bytes, caller-owned, 4-byte
+ *               aligned; its contents on entry do not matter and are
+ *               overwritten (calls that share one workspace must not overlap)
+ * Requires T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 16), rows <= 2^31 - 1,
+ * 4-byte aligned pointers.  Returns FP8Q_ERR_WORKSPACE when workspace_bytes is
+ * smaller than fp8q_moe_route_workspace_bytes(T, E).  Three launches on
+ * `stream`; deterministic. */
+int fp8q_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_idx, int32_t *offsets,
+                        int32_t *row_of, int32_t *row_token, int64_t rows, void *workspace, int64_t workspace_bytes,
+                        void *stream);
+
+/* Expert-sorted FP8 activations for the grouped GEMM (FP8 dispatch): for every
+ * row r < min(offsets[E], rows),
+ *   qa[r, :] = q[row_token[r], :],  sa[kb][r] = s[kb][row_token[r]]
+ * or zero codes and scale 0 when row_token[r] is -1 (or outside [0, T)).
+ *   q  : E4M3 [T, K], s : fp32 [K/128][T]   (fp8q_quant_act_1x128 of the tokens)
+ *   row_of [T][k], row_token [rows], offsets [E+1] : the outputs of one
+ *        fp8q_moe_route_topk call (device); the codes of a token's rows are
+ *        written through row_of (each token row is read once), the scales and
+ *        the empty rows through row_token, so the two must describe the same
+ *        layout
+ *   qa : E4M3 [rows, K], sa : fp32 [K/128][rows]   (outputs)
+ * Rows from offsets[E] on are not written.  Gathering quantized rows equals
+ * quantizing gathered bf16 rows bit for bit (a 1x128 group lies in one row).
+ * Requires 0 <= T <= 2^31 - 1, K % 128 == 0, k >= 1 with T*k < 2^31, E >= 1,
+ * 0 <= rows <= 2^31 - 1; q and qa 16-byte aligned, the other pointers 4-byte
+ * aligned.  q, s and row_of may be NULL when T == 0.  One launch. */
+int fp8q_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K, int64_t k, const int32_t *row_of,
+                        const int32_t *row_token, const int32_t *offsets, int64_t E, int64_t rows, uint8_t *qa,
+                        float *sa, void *stream);
 
 #ifdef __cplusplus
 }

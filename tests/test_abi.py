@@ -22,13 +22,15 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(fp8q_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(fp8q_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8q_quant_act_1x128", "fp8q_quant_w_128x128", "fp8q_gemm_blockscaled",
-              "fp8q_grouped_gemm_blockscaled", "fp8q_dequant_w_128x128", "fp8q_status_string", "fp8q_version"):
+              "fp8q_grouped_gemm_blockscaled", "fp8q_dequant_w_128x128", "fp8q_moe_route_capacity",
+              "fp8q_moe_route_workspace_bytes", "fp8q_moe_route_topk", "fp8q_moe_gather_fp8",
+              "fp8q_status_string", "fp8q_version"):
         assert n in names
 
 
@@ -44,7 +46,7 @@ def test_library_contains_gfx950_code():
 
 def test_status_strings(lib):
     assert lib.fp8q_version() >= 100
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert lib.fp8q_status_string(code).decode().startswith("FP8Q_")
     assert b"unknown" in lib.fp8q_status_string(42)
 
@@ -82,6 +84,40 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_dequant_w_128x128(A, None, 128, 128, B, None) == -1
     assert lib.fp8q_dequant_w_128x128(A, B, 128, 128, MIS, None) == -3
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, MIS, 0, 4, 128, 128, None) == -3
+
+
+def test_moe_routing_sizes_and_validation(lib):
+    import oracle
+    lib.fp8q_moe_route_capacity.restype = ctypes.c_int64
+    lib.fp8q_moe_route_capacity.argtypes = [ctypes.c_int64] * 3
+    lib.fp8q_moe_route_workspace_bytes.restype = ctypes.c_int64
+    lib.fp8q_moe_route_workspace_bytes.argtypes = [ctypes.c_int64] * 2
+    I = ctypes.c_int64
+    for T, E, k in ((8192, 64, 8), (0, 1, 1), (5, 256, 8), (1000, 1024, 16)):
+        assert lib.fp8q_moe_route_capacity(T, E, k) == oracle.moe_route_capacity(T, E, k)
+        assert lib.fp8q_moe_route_workspace_bytes(T, E) == 4 * E * ((T + 63) // 64)
+    for T, E, k in ((-1, 8, 2), (8, 0, 1), (8, 1025, 2), (8, 8, 9), (8, 32, 17), (8, 8, 0)):
+        assert lib.fp8q_moe_route_capacity(T, E, k) == -1
+    cap = lib.fp8q_moe_route_capacity(100, 8, 2)
+    route = lib.fp8q_moe_route_topk
+    route.argtypes = [ctypes.c_void_p, I, I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      I, ctypes.c_void_p, I, ctypes.c_void_p]
+    assert route(A, 100, 8, 9, A, A, A, A, cap, A, 4096, None) == -2            # k > E
+    assert route(A, 100, 8, 2, A, A, A, A, cap - 1, A, 4096, None) == -2        # rows below the capacity
+    assert route(A, 100, 8, 2, A, None, A, A, cap, A, 4096, None) == -1
+    assert route(A, 100, 8, 2, A, A, A, A, cap, None, 4096, None) == -1
+    assert route(MIS, 100, 8, 2, A, A, A, A, cap, A, 4096, None) == -3
+    assert route(A, 100, 8, 2, A, A, A, A, cap, A, 4 * 8 * 2 - 1, None) == -8    # workspace too small
+    gather = lib.fp8q_moe_gather_fp8
+    gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, I, I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert gather(A, A, 4, 100, 2, A, A, A, 8, 512, B, B, None) == -2                 # K not a multiple of 128
+    assert gather(A, A, 4, 128, 2, A, A, A, 0, 512, B, B, None) == -2                 # E < 1
+    assert gather(A, A, 4, 128, 0, A, A, A, 8, 512, B, B, None) == -2                 # k < 1
+    assert gather(None, None, 4, 128, 2, None, None, None, 8, 0, None, None, None) == 0   # no rows
+    assert gather(None, A, 4, 128, 2, A, A, A, 8, 512, B, B, None) == -1
+    assert gather(A, A, 4, 128, 2, None, A, A, 8, 512, B, B, None) == -1              # row_of
+    assert gather(A, A, 4, 128, 2, A, A, A, 8, 512, MIS, B, None) == -3
 
 
 def test_valid_call_without_gpu_reports_no_device(lib):

@@ -211,8 +211,11 @@ def test_grouped_full_moe_sampled():
     """The full MoE layer: 8192 tokens, top-8 of 64 experts, expert weights [2048, 7168]; sampled rows
     from every expert segment (first, last routed row and a random one), all 2048 columns."""
     d = wl.moe()
-    r = d["routing"]
-    say(f"grouped gemm: full moe M_total={d['M']} (counts {r.counts.min()}..{r.counts.max()})")
+    r = oracle.moe_route_topk(d["logits"], d["topk"])       # the expert-sorted layout, from the oracle
+    a = np.zeros((r.M, d["K"]), np.uint16)
+    a[r.row_token >= 0] = d["tokens"][r.row_token[r.row_token >= 0]]
+    d["a"] = a
+    say(f"grouped gemm: full moe M_total={r.M} (counts {r.counts.min()}..{r.counts.max()})")
     qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(d["a"]))
     qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(d["w"]))
     c = gemm_out_to_f64(fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(r.offsets).cuda()))

@@ -1,0 +1,143 @@
+"""GPU parity of the MoE routing (top-k gating and the expert-sorted, 128-padded layout) and of the FP8 row
+gather with the oracle: bit-exact, since both are integer and byte work.  Then the whole dispatch path at the
+MoE layer's size (quantize tokens, route, gather, grouped GEMM) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_quantization_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import assert_gemm_within_bound, bf16_dev, f32_dev, gemm_out_to_f64, host, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_route(logits, k, rows):
+    """Routes on the GPU with every output and the workspace pre-filled with garbage."""
+    T, E = logits.shape
+    ws_bytes = fq.load_library().fp8q_moe_route_workspace_bytes(T, E)
+    ws = torch.full((max(ws_bytes, 4),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = tuple(torch.full(shape, -7, dtype=torch.int32, device="cuda")
+                for shape in ((T, k), (E + 1,), (T, k), (rows,)))
+    fq.fp8q_moe_route_topk(f32_dev(logits), k, rows=rows, workspace=ws, out=out)
+    return [host(t) for t in out]
+
+
+def check_route(logits, k, what, rows=None):
+    T, E = logits.shape
+    rows = oracle.moe_route_capacity(T, E, k) if rows is None else rows
+    say(f"route: {what} T={T} E={E} k={k} rows={rows}")
+    got = gpu_route(logits, k, rows)
+    r = oracle.moe_route_topk(logits, k, rows=rows)
+    for name, g, o in zip(("topk_idx", "offsets", "row_of", "row_token"), got,
+                          (r.topk_idx, r.offsets, r.row_of, r.row_token)):
+        bad = np.argwhere(g != o)
+        assert bad.size == 0, f"{what}: {name} differs at {len(bad)} places, first {tuple(bad[0])}"
+    return r
+
+
+def logits_of(kind, T, E, seed):
+    g = np.random.default_rng([21, seed])
+    if kind == "ties":       # five values including both zeros: most rows hold ties
+        vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)
+        return vals[g.integers(0, len(vals), size=(T, E))]
+    x = g.standard_normal((T, E), dtype=np.float32)
+    if kind == "skew":       # experts 0 and 1 win for most tokens; most others are empty
+        x[: (T * 2) // 3, :2] += 10.0
+    return x
+
+
+def test_route_moe_layer_logits():
+    d = wl.moe(with_weights=False)
+    r = check_route(d["logits"], d["topk"], "moe layer")
+    say(f"  rows used {r.M}, counts {r.counts.min()}..{r.counts.max()}")
+
+
+@pytest.mark.parametrize("T,E,k,kind", [
+    (1000, 256, 8, "normal"),    # 256 routed experts, top-8
+    (777, 64, 8, "ties"),        # ragged last chunk, tie-heavy
+    (300, 64, 8, "skew"),        # empty experts and 2-segment skew
+    (1, 4, 2, "normal"),
+    (0, 8, 2, "normal"),         # no tokens: offsets 0, every row empty
+    (65, 16, 16, "ties"),        # k = 16 (the 16-entry list), k = E
+    (129, 33, 9, "normal"),      # odd E, k = 9
+    (130, 1024, 3, "normal"),    # the largest E
+    (100, 64, 1, "ties"),        # k = 1
+])
+def test_route_matches_oracle(T, E, k, kind):
+    check_route(logits_of(kind, T, E, T + E + k), k, f"{kind}")
+
+
+def test_route_rows_past_capacity_are_empty_and_calls_repeat():
+    lg = logits_of("normal", 500, 64, 5)
+    cap = oracle.moe_route_capacity(500, 64, 8)
+    check_route(lg, 8, "rows past capacity", rows=cap + 300)
+    a = gpu_route(lg, 8, cap)
+    b = gpu_route(lg, 8, cap)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("T,K,E,k", [(1000, 512, 64, 8), (5, 128, 4, 2), (0, 256, 8, 2), (300, 7168, 64, 8)])
+def test_gather_matches_oracle(T, K, E, k):
+    """Random codes and scales, the oracle's layout; rows at or past offsets[E] must keep their contents."""
+    g = np.random.default_rng([22, T, K])
+    q = g.integers(0, 256, size=(T, K), dtype=np.uint8)
+    s = g.uniform(1e-4, 1.0, size=(K // 128, T)).astype(np.float32)
+    cap = oracle.moe_route_capacity(T, E, k)
+    r = oracle.moe_route_topk(logits_of("normal", T, E, 3), k, rows=cap)
+    say(f"gather: T={T} K={K} E={E} k={k} rows {r.M} of {cap}")
+    qa = torch.full((cap, K), 0xCD, dtype=torch.uint8, device="cuda")
+    sa = torch.full((K // 128, cap), -3.0, dtype=torch.float32, device="cuda")
+    row_of = torch.from_numpy(r.row_of.reshape(T, k)).cuda()
+    fq.fp8q_moe_gather_fp8(u8_dev(q), f32_dev(s), row_of, torch.from_numpy(r.row_token).cuda(),
+                           torch.from_numpy(r.offsets).cuda(), qa, sa)
+    gq, gs = host(qa), host(sa)
+    oq, os_ = oracle.moe_gather_fp8(q, s, r.row_token)
+    used = r.M
+    assert np.array_equal(gq[:used], oq[:used])
+    assert np.array_equal(gs[:, :used].view(np.uint32), os_[:, :used].view(np.uint32))
+    assert np.all(gq[used:] == 0xCD) and np.all(gs[:, used:] == -3.0)
+
+
+def test_full_dispatch_path_of_the_moe_layer():
+    """8192 tokens x 7168 quantized, routed top-8 of 64 and gathered on the GPU (bit-exact with the oracle's
+    quantizer, routing and gather), then the grouped GEMM over the routing capacity: sampled rows of every
+    expert segment within the GEMM bound, padding rows exactly 0, rows past the layout untouched."""
+    d = wl.moe()
+    T, E, k, N, K = d["T"], d["E"], d["topk"], d["N"], d["K"]
+    cap = fq.fp8q_moe_route_capacity(T, E, k)
+    say(f"moe dispatch: T={T} E={E} k={k} K={K}, capacity {cap} rows")
+    qt, st = fq.fp8q_quant_act_1x128(bf16_dev(d["tokens"]))
+    topk_idx, off, row_of, row_token = fq.fp8q_moe_route_topk(f32_dev(d["logits"]), k)
+    qa, sa = fq.fp8q_moe_gather_fp8(qt, st, row_of, row_token, off)
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(d["w"]))
+    c = torch.full((cap, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, off, c=c)
+
+    oqt, ost = oracle.quant_act_1x128(d["tokens"])
+    r = oracle.moe_route_topk(d["logits"], k, rows=cap)
+    assert np.array_equal(host(topk_idx), r.topk_idx) and np.array_equal(host(off), r.offsets)
+    assert np.array_equal(host(row_of), r.row_of) and np.array_equal(host(row_token), r.row_token)
+    used = r.M
+    oqa, osa = oracle.moe_gather_fp8(oqt, ost, r.row_token[:used])
+    assert np.array_equal(host(qa)[:used], oqa)
+    assert np.array_equal(host(sa)[:, :used].view(np.uint32), osa.view(np.uint32))
+    say(f"  quantize + route + gather bit-exact over {used} rows")
+
+    oqw, osw = oracle.quant_w_128x128(d["w"])
+    g = np.random.default_rng(4)
+    counts = r.counts
+    rows = []
+    for e in range(E):
+        lo, cnt = int(r.offsets[e]), int(counts[e])
+        if cnt:
+            rows += [lo, lo + cnt - 1, lo + int(g.integers(cnt))]
+    rows = np.array(sorted(set(rows)))
+    C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, r.offsets, rows=rows)
+    ch = gemm_out_to_f64(c)
+    ratio = assert_gemm_within_bound(ch[rows], C, B, True, "moe dispatch")
+    empty = np.nonzero(r.row_token[:used] < 0)[0]
+    assert np.all(ch[empty] == 0.0)
+    assert np.all(np.isnan(ch[used:]))
+    say(f"  grouped GEMM max err/bound {ratio:.3g}")

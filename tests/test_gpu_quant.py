@@ -121,12 +121,17 @@ def test_act_full_workloads(name):
 
 
 def test_act_moe_padded_tokens():
+    """The 1x128 quantizer on the MoE layer's expert-sorted, 128-padded bf16 rows (layout from the oracle's
+    routing); empty rows must give code 0 and scale 0."""
     d = wl.moe(with_weights=False)
-    say(f"act quant: moe padded tokens {d['a'].shape}")
-    q, s = gpu_act(d["a"])
-    oq, os_ = oracle.quant_act_1x128(d["a"])
+    r = oracle.moe_route_topk(d["logits"], d["topk"])
+    a = np.zeros((r.M, d["K"]), np.uint16)
+    a[r.row_token >= 0] = d["tokens"][r.row_token[r.row_token >= 0]]
+    say(f"act quant: moe padded tokens {a.shape}")
+    q, s = gpu_act(a)
+    oq, os_ = oracle.quant_act_1x128(a)
     assert_same(q, s, oq, os_, "moe tokens")
-    pad = d["routing"].row_token < 0
+    pad = r.row_token < 0
     assert np.all(q[pad] == 0) and np.all(s[:, pad] == 0)
 
 

@@ -2,9 +2,10 @@
 
 This module is shared by the tests, the benchmark and the smoke check; it feeds
 the CPU oracle and the HIP library the same host bytes.  It holds none of the
-method's arithmetic (no amax, no scale, no FP8 encoding, no GEMM): it only draws
-random numbers, rounds them to bf16 as input data, and lays tokens out per
-expert for the MoE case.
+method's arithmetic (no amax, no scale, no FP8 encoding, no GEMM, no routing): it
+only draws random numbers and rounds them to bf16 as input data.  For the MoE
+case it supplies tokens, router logits and expert weights; choosing each
+token's experts and laying the tokens out per expert are steps of the method.
 
 Generator: numpy PCG64 seeded with ``[workload_seed, tensor_id]``.  Normal draws
 are float32, scaled in float32, then rounded to bf16 (round-to-nearest-even,
@@ -19,14 +20,13 @@ deepinsightai.io page):
   tiny    A [128, 512] ~ N(0,1), 4 channels x50; W [256, 512] ~ N(0, 0.02)       seed 0
   up      A [4096, 7168] ~ N(0,1), 72 (1%) channels x20; W [18432, 7168]         seed 1
   down    A = bf16(SiLU(x) * y) [4096, 18432], x, y ~ N(0,1); W [7168, 18432]    seed 2
-  moe     8192 tokens x 7168 ~ N(0,1); router logits [8192, 64] ~ N(0,1); top-8;
-          per-expert W [64][2048, 7168] ~ N(0, 0.02); segments padded to 128      seed 3
+  moe     8192 tokens x 7168 ~ N(0,1); router logits [8192, 64] ~ N(0,1) (routed
+          top-8, segments padded to 128 rows); W [64][2048, 7168] ~ N(0, 0.02)   seed 3
   decode  A [64, 7168] ~ N(0,1); W pre-quantized: E4M3 codes uniform over the 254
           finite codes, 128x128 fp32 scales ~ U(1e-4, 1e-2)                        seed 4
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
 
 import numpy as np
 
@@ -107,53 +107,6 @@ def uniform_f32(seed, tid, shape, lo, hi):
 
 
 # ---------------------------------------------------------------------------
-# MoE routing (input structure, not part of the quantize/GEMM method)
-# ---------------------------------------------------------------------------
-
-@dataclass
-class Routing:
-    """Token -> expert layout for the grouped GEMM.
-
-    ``offsets[e]..offsets[e+1]`` are the padded rows of expert ``e``; ``row_token[r]`` is the token
-    that padded row ``r`` carries, or -1 for a padding row (all-zero activations).
-    """
-    counts: np.ndarray          # int64 [E] routed tokens per expert
-    offsets: np.ndarray         # int32 [E+1], multiples of `pad`
-    row_token: np.ndarray       # int64 [offsets[-1]]
-    topk_idx: np.ndarray = field(repr=False)  # int64 [T, k]
-
-
-def route_topk(logits: np.ndarray, k: int, pad: int = 128) -> Routing:
-    """Top-k experts per token by logit (ties to the lower expert index); per-expert segments list
-    their tokens in ascending order and are padded with empty rows to a multiple of ``pad``."""
-    T, E = logits.shape
-    # stable sort on -logit keeps the lower index first among equal logits
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
-    counts = np.bincount(order.ravel(), minlength=E).astype(np.int64)
-    padded = ((counts + pad - 1) // pad) * pad
-    offsets = np.zeros(E + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(padded)
-    row_token = np.full(int(offsets[-1]), -1, dtype=np.int64)
-    tok = np.repeat(np.arange(T, dtype=np.int64), k)
-    exp = order.ravel()
-    srt = np.lexsort((tok, exp))  # by expert, then token ascending
-    tok, exp = tok[srt], exp[srt]
-    starts = np.zeros(E, dtype=np.int64)
-    starts[1:] = np.cumsum(counts)[:-1]
-    within = np.arange(len(tok), dtype=np.int64) - starts[exp]
-    row_token[offsets[exp] + within] = tok
-    return Routing(counts=counts, offsets=offsets.astype(np.int32), row_token=row_token, topk_idx=order)
-
-
-def gather_rows(tokens_bits: np.ndarray, row_token: np.ndarray) -> np.ndarray:
-    """Expert-sorted padded activation matrix: row r is token row_token[r], or zeros when -1."""
-    out = np.zeros((len(row_token), tokens_bits.shape[1]), dtype=np.uint16)
-    valid = row_token >= 0
-    out[valid] = tokens_bits[row_token[valid]]
-    return out
-
-
-# ---------------------------------------------------------------------------
 # The five workloads
 # ---------------------------------------------------------------------------
 
@@ -183,9 +136,7 @@ def moe(T=8192, K=7168, E=64, k=8, N=2048, with_weights=True):
     s = SEEDS["moe"]
     tokens = normal_bf16(s, T_A, (T, K))
     logits = rng(s, T_LOGITS).standard_normal((T, E), dtype=np.float32)
-    r = route_topk(logits, k)
-    d = {"name": "moe", "tokens": tokens, "logits": logits, "routing": r, "a": gather_rows(tokens, r.row_token),
-         "M": int(r.offsets[-1]), "N": N, "K": K, "E": E, "T": T, "topk": k}
+    d = {"name": "moe", "tokens": tokens, "logits": logits, "M": None, "N": N, "K": K, "E": E, "T": T, "topk": k}
     if with_weights:
         d["w"] = normal_bf16(s, T_W, (E, N, K), 0.02)
     return d
