@@ -307,27 +307,44 @@ struct TileLoader {
     }
 };
 
-// Tile coordinates of workgroup t for a dense n_mt x n_nt tile grid.  Workgroups are dispatched to the 8 XCDs
-// round-robin (t % 8), and 256 of them (one per CU) run at a time.  Each run of 256 covers a 16 x 16 square of
-// tiles ("supergroup"), and within it XCD x takes a 4 (M) x 8 (N) block, so the 32 tiles resident on one XCD
-// share 4 activation and 8 weight tile rows in that XCD's L2, and the XCDs together share the square's operands
-// in the Infinity Cache.  Returns false for indices that fall outside the grid.
-__device__ __forceinline__ bool supergroup_tile(int64_t t, int64_t n_mt, int64_t n_nt, int64_t &mt, int64_t &nt) {
-    const int64_t sg = t / 256, j = t % 256;
-    const int64_t x = j % 8, k = j / 8;  // XCD, position within the XCD's 4 x 8 block
-    const int64_t sg_m = (n_mt + 15) / 16;
-    const int64_t sgm = sg % sg_m, sgn = sg / sg_m;
-    mt = sgm * 16 + (x % 4) * 4 + (k % 4);
-    nt = sgn * 16 + (x / 4) * 8 + (k / 4);
-    return mt < n_mt && nt < n_nt;
+// Workgroups are dispatched to the 8 XCDs round-robin (t % 8), 256 of them (one per CU) at a time.  This
+// permutation gives XCD x the 32 consecutive indices [256 r + 32 x, +32) of each round r of 256; it is a
+// bijection on every whole round.
+__device__ __forceinline__ int64_t xcd_order(int64_t t) { return (t / 256) * 256 + (t % 8) * 32 + (t % 256) / 8; }
+
+// Tile (mt, nt) of the i-th tile of a dense n_mt x n_nt grid, in an order made for the XCD permutation above:
+// columns of 16 N tiles ("supergroup columns", the last may be narrower), each cut into supergroups of 16 M
+// tiles (the last may be shorter), each enumerated as 8-wide sub-block columns of 4-high sub-blocks, M
+// fastest.  Only tiles inside the grid are enumerated, so every round of 256 indices is 256 tiles whatever the
+// grid's shape.  In a full 16 x 16 supergroup each XCD's 32 tiles form a 4 (M) x 8 (N) block sharing 4
+// activation and 8 weight tile rows in that XCD's L2, and a round's 16 x 16 square shares its operands in the
+// Infinity Cache.  Returns false past the last tile.
+__device__ __forceinline__ bool dense_tile_at(int64_t i, int64_t n_mt, int64_t n_nt, int64_t &mt, int64_t &nt) {
+    if (i >= n_mt * n_nt) return false;
+    const int64_t colw = 16 * n_mt;
+    const int64_t sgn = i / colw;
+    const int64_t hn = n_nt - 16 * sgn < 16 ? n_nt - 16 * sgn : 16;
+    int64_t j = i - sgn * colw;
+    const int64_t sgm = j / (16 * hn);
+    const int64_t hm = n_mt - 16 * sgm < 16 ? n_mt - 16 * sgm : 16;
+    j -= sgm * 16 * hn;
+    const int64_t qn = j / (8 * hm);
+    const int64_t wq = hn - 8 * qn < 8 ? hn - 8 * qn : 8;
+    j -= qn * 8 * hm;
+    const int64_t qm = j / (4 * wq);
+    const int64_t hq = hm - 4 * qm < 4 ? hm - 4 * qm : 4;
+    j -= qm * 4 * wq;
+    mt = 16 * sgm + 4 * qm + j % hq;
+    nt = 16 * sgn + 8 * qn + j / hq;
+    return true;
 }
 
-// Coordinates of dense tile t (supergroup order over an n_mtiles x n_ntiles grid of 256 x bn tiles whose
-// columns start at n_begin).  Returns false for indices outside the grid.
-__device__ __forceinline__ bool dense_tile(int64_t t, int64_t n_begin, int64_t n_mtiles, int64_t n_ntiles, int64_t bn,
+// Coordinates of dense tile i (over an n_mtiles x n_ntiles grid of 256 x bn tiles whose columns start at
+// n_begin).  Returns false past the last tile.
+__device__ __forceinline__ bool dense_tile(int64_t i, int64_t n_begin, int64_t n_mtiles, int64_t n_ntiles, int64_t bn,
                                            int64_t &m0, int64_t &n0) {
     int64_t mt, nt;
-    if (!supergroup_tile(t, n_mtiles, n_ntiles, mt, nt)) return false;
+    if (!dense_tile_at(i, n_mtiles, n_ntiles, mt, nt)) return false;
     m0 = mt * kBig;
     n0 = n_begin + nt * bn;
     return true;
@@ -341,7 +358,7 @@ __device__ __forceinline__ bool dense_tile(int64_t t, int64_t n_begin, int64_t n
 __device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restrict__ off, int64_t E, int64_t M,
                                              int64_t n_mtiles, int64_t n_ntiles, int64_t bn, int lane, int64_t &m0,
                                              int64_t &mend, int64_t &n0, int64_t &e) {
-    const int64_t T = (t / 256) * 256 + (t % 8) * 32 + (t % 256) / 8;
+    const int64_t T = xcd_order(t);
     const int64_t mt = T / n_ntiles;  // n_mtiles is an upper bound on the number of M tiles
     if (mt >= n_mtiles) return false;
     n0 = (T % n_ntiles) * bn;
@@ -518,10 +535,10 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
     }
 }
 
-// Large-M GEMM.  Dense: workgroups [0, main_blocks) cover columns [0, n_tail) with 256 x (32 NSUB) tiles;
-// when NSUB_TAIL != 0 the workgroups after them cover columns [n_tail, N) with narrower 256 x (32 NSUB_TAIL)
-// tiles, which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of
-// the last round.  Grouped (NSUB = 8): one 256 x 256 tile per workgroup, or 128 x 256 where a segment has
+// Large-M GEMM.  Dense: tiles [0, main_tiles) cover columns [0, n_tail) with 256 x (32 NSUB) tiles; when
+// NSUB_TAIL != 0 the tiles after them cover columns [n_tail, N) with narrower 256 x (32 NSUB_TAIL) tiles,
+// which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of the
+// last round.  Grouped (NSUB = 8): one 256 x 256 tile per workgroup, or 128 x 256 where a segment has
 // only 128 rows left.
 template <bool OUT_BF16, bool GROUPED, int NSUB, int NSUB_TAIL>
 __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
@@ -530,7 +547,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
                                                              const float *__restrict__ sw, void *__restrict__ c,
                                                              int64_t M, int64_t N, int64_t K,
                                                              const int32_t *__restrict__ off, int64_t E,
-                                                             int64_t n_mtiles, int64_t n_ntiles, int64_t main_blocks,
+                                                             int64_t n_mtiles, int64_t n_ntiles, int64_t main_tiles,
                                                              int64_t n_tail, int64_t n_ntiles_tail) {
     constexpr int kMain = TileLoader<32 * NSUB>::kStageBytes;
     constexpr int kTail = TileLoader<32 * (NSUB_TAIL ? NSUB_TAIL : NSUB)>::kStageBytes;
@@ -550,14 +567,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
             bs_tile<OUT_BF16, NSUB, 2>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0);
         return;
     }
+    // Dense: the main tiles, then (NSUB_TAIL != 0) the narrower tail tiles, as one sequence of tiles in XCD
+    // order, so the tail tiles fill the main tiles' last round.
+    const int64_t i = xcd_order(t);
     if constexpr (NSUB_TAIL != 0) {
-        if (t >= main_blocks) {
-            if (!dense_tile(t - main_blocks, n_tail, n_mtiles, n_ntiles_tail, 32 * NSUB_TAIL, m0, n0)) return;
+        if (i >= main_tiles) {
+            if (!dense_tile(i - main_tiles, n_tail, n_mtiles, n_ntiles_tail, 32 * NSUB_TAIL, m0, n0)) return;
             bs_tile<OUT_BF16, NSUB_TAIL, 2>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, m0, M, n0);
             return;
         }
     }
-    if (!dense_tile(t, 0, n_mtiles, n_ntiles, 32 * NSUB, m0, n0)) return;
+    if (!dense_tile(i, 0, n_mtiles, n_ntiles, 32 * NSUB, m0, n0)) return;
     bs_tile<OUT_BF16, NSUB, 2>(stage0, stage1, qa, sa, qw, sw, c, M, N, K, m0, M, n0);
 }
 
@@ -625,22 +645,19 @@ Plan256 plan_256(int64_t M, int64_t N, int64_t ncu) {
     return best;
 }
 
-// Workgroups of a dense n_mt x n_nt grid in supergroup order (16 x 16 squares; indices outside the grid exit).
-static int64_t supergroup_blocks(int64_t n_mt, int64_t n_nt) { return ((n_mt + 15) / 16) * ((n_nt + 15) / 16) * 256; }
 
 template <bool OUT_BF16, int NSUB, int NSUB_TAIL>
 hipError_t launch_256_dense(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                             int64_t M, int64_t N, int64_t K, int64_t n_tail, hipStream_t stream) {
     const int64_t n_mt = (M + kBig - 1) / kBig;
     const int64_t n_nt = (n_tail + 32 * NSUB - 1) / (32 * NSUB);
-    const int64_t main_blocks = supergroup_blocks(n_mt, n_nt);
-    int64_t n_nt_tail = 0, blocks = main_blocks;
-    if (NSUB_TAIL != 0) {
-        n_nt_tail = (N - n_tail + 32 * NSUB_TAIL - 1) / (32 * NSUB_TAIL);
-        blocks += supergroup_blocks(n_mt, n_nt_tail);
-    }
+    const int64_t main_tiles = n_mt * n_nt;
+    const int64_t n_nt_tail = NSUB_TAIL != 0 ? (N - n_tail + 32 * NSUB_TAIL - 1) / (32 * NSUB_TAIL) : 0;
+    // whole rounds of 256 workgroups (the XCD permutation is a bijection on each); indices past the last
+    // tile exit at once
+    const int64_t blocks = (main_tiles + n_mt * n_nt_tail + 255) / 256 * 256;
     gemm_bs_256_kernel<OUT_BF16, false, NSUB, NSUB_TAIL><<<dim3((unsigned)blocks), 512, 0, stream>>>(
-        qa, sa, qw, sw, c, M, N, K, nullptr, 0, n_mt, n_nt, main_blocks, n_tail, n_nt_tail);
+        qa, sa, qw, sw, c, M, N, K, nullptr, 0, n_mt, n_nt, main_tiles, n_tail, n_nt_tail);
     return hipGetLastError();
 }
 

@@ -304,13 +304,14 @@ hipError_t launch_moe_route_topk(const float *logits, int64_t T, int E, int k, i
                                                                       workspace);
     }
     moe_scan_kernel<<<1, 1024, 0, stream>>>(workspace, C, E, offsets, row_token, rows);
-    if (C > 0)
+    if (C > 0) {
         if (k <= 8)
             moe_assign_kernel<8><<<dim3((unsigned)C), 64, 0, stream>>>(topk_idx, workspace, T, E, k, row_of,
                                                                        row_token, rows);
         else
             moe_assign_kernel<16><<<dim3((unsigned)C), 64, 0, stream>>>(topk_idx, workspace, T, E, k, row_of,
                                                                         row_token, rows);
+    }
     return hipGetLastError();
 }
 

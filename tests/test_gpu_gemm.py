@@ -235,6 +235,23 @@ def test_grouped_full_moe_sampled():
     say(f"  max err/bound {ratio:.3g}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1280, 2048, 256), (4352, 1024, 256), (768, 4096, 384), (8960, 2816, 128)],
+                         ids=["5x8_tiles", "17x4_tiles", "3x16_tiles", "35x11_tiles"])
+def test_tile_grids_that_are_not_whole_supergroups(M, N, K):
+    """Every output of grids whose tile counts are not multiples of 16 (partial 16 x 16 supergroups in M, in
+    N or both): the tile order must still cover each tile once."""
+    g = np.random.default_rng(M * 7 + N)
+    a = g.standard_normal((M, K)).astype(np.float32)
+    w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    ab, wb = wl.bf16_bits(a), wl.bf16_bits(w)
+    say(f"gemm tile grid: M={M} N={N} K={K}")
+    c = gemm_out_to_f64(gpu_path(ab, wb, "f32"))
+    qa, sa = oracle.quant_act_1x128(ab)
+    qw, sw = oracle.quant_w_128x128(wb)
+    C, B = oracle.gemm_blockscaled(qa, sa, qw, sw)
+    assert_gemm_within_bound(c, C, B, False, f"{M}x{N}")
+
+
 @pytest.mark.parametrize("M,N,K", [(2304, 7168, 256), (2048, 7168, 256), (300, 640, 1024), (4096, 7168, 256),
                                    (1024, 18432, 256)],
                          ids=["w256", "w224", "w192", "w256+tail192", "w192+tail128"])
