@@ -559,6 +559,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
     if constexpr (GROUPED) {
         int64_t e = 0;
         if (!grouped_tile(t, off, E, M, n_mtiles, n_ntiles, 32 * NSUB, threadIdx.x & 63, m0, mend, n0, e)) return;
+        // The expert and the row range are the same in every lane, but they come out of lane shuffles, so the
+        // compiler cannot prove it; without these the buffer descriptors built from them would sit in VGPRs and
+        // every buffer load of the main loop would be wrapped in a loop over distinct descriptor values.
+        e = __builtin_amdgcn_readfirstlane((int)e);
+        m0 = __builtin_amdgcn_readfirstlane((int)m0);
+        mend = __builtin_amdgcn_readfirstlane((int)mend);
         const uint8_t *W = qw + e * N * K;
         const float *SW = sw + e * (N / 128) * (K >> 7);
         if (mend - m0 <= 128)  // a segment's last 128 rows: the 128 x 256 layout does no work on absent rows
