@@ -75,6 +75,8 @@ def load(path: str | None = None):
         lib.oracle_moe_route_topk.restype = ctypes.c_int
         lib.oracle_moe_gather_fp8.argtypes = [P, P, I64, I64, P, I64, P, P]
         lib.oracle_moe_gather_fp8.restype = ctypes.c_int
+        lib.oracle_swiglu_bf16.argtypes = [P, P, I64, P, P]
+        lib.oracle_swiglu_bf16.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -307,3 +309,73 @@ def moe_gather_fp8(q, s, row_token, lib=None):
     _check(lib.oracle_moe_gather_fp8(_ptr(q), _ptr(s), T, K, _ptr(row_token), rows, _ptr(qa), _ptr(sa)),
            "moe_gather_fp8")
     return qa, sa
+
+
+# ---------------------------------------------------------------------------
+# Fused SwiGLU + 1x128 quantization
+# ---------------------------------------------------------------------------
+
+def _bf16_exact(bits: int):
+    from decimal import Decimal
+    return Decimal(float(np.array([int(bits) << 16], dtype=np.uint32).view(np.float32)[0]))
+
+
+def swiglu_exact_bf16(xb: int, yb: int) -> int:
+    """bf16(SiLU(x) * y) for one pair of bf16 bit patterns, from 80-digit decimal arithmetic (exp correctly
+    rounded at that precision): the settlement of the values the C evaluation flags as too close to a
+    rounding midpoint to decide in double."""
+    from decimal import Decimal, localcontext, ROUND_FLOOR
+    with localcontext() as ctx:
+        ctx.prec = 80
+        x, y = _bf16_exact(xb), _bf16_exact(yb)
+        # the same value in a form whose exponential cannot overflow
+        v = x * y / (1 + (-x).exp()) if x >= 0 else x * y * x.exp() / (1 + x.exp())
+        neg = (v < 0) or (v == 0 and ((xb ^ yb) & 0x8000))
+        a = abs(v)
+        if a == 0:
+            return 0x8000 if neg else 0
+        ex = int(float(a).hex().split("p")[1]) if float(a) != 0 else -1000
+        # the binade of a (its double is within 1e-60 relative; a power of two is itself a bf16 value)
+        while Decimal(2) ** ex > a:
+            ex -= 1
+        while Decimal(2) ** (ex + 1) <= a:
+            ex += 1
+        ex = max(ex, -126)
+        ulp = Decimal(2) ** (ex - 7)
+        q = a / ulp
+        fl = q.to_integral_value(rounding=ROUND_FLOOR)
+        rem = q - fl
+        if abs(rem - Decimal("0.5")) <= Decimal(10) ** -60:
+            # Not decided at 80 digits: only possible when e^-x vanished next to 1 (x huge) and x*y is the
+            # midpoint itself; the true value x*y / (1 + e^-x) then lies just inside it (towards zero).
+            assert x > 0 and abs(x * y) == (fl + Decimal("0.5")) * ulp, "an undecided value SiLU cannot give"
+        elif rem > Decimal("0.5"):
+            fl += 1
+        r = float(fl * ulp)
+    bits = int(np.array([r], dtype=np.float32).view(np.uint32)[0]) >> 16
+    return bits | (0x8000 if neg else 0)
+
+
+def swiglu_bf16(x_bits, y_bits, lib=None, return_flags=False):
+    """h = bf16(SiLU(x) * y) elementwise (the exact value rounded once to nearest even), bf16 in and out as
+    uint16 bit patterns of one shape.  Values the C evaluation cannot decide in double are settled by
+    :func:`swiglu_exact_bf16`."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    y = _c(y_bits, np.uint16)
+    assert x.shape == y.shape
+    h = np.empty(x.shape, dtype=np.uint16)
+    amb = np.zeros(x.shape, dtype=np.uint8)
+    _check(lib.oracle_swiglu_bf16(_ptr(x), _ptr(y), x.size, _ptr(h), _ptr(amb)), "swiglu_bf16")
+    flat = np.flatnonzero(amb)
+    hf = h.reshape(-1)
+    for i in flat:
+        hf[i] = swiglu_exact_bf16(int(x.reshape(-1)[i]), int(y.reshape(-1)[i]))
+    return (h, amb.astype(bool)) if return_flags else h
+
+
+def swiglu_quant_1x128(x_bits, y_bits, lib=None):
+    """Fused SwiGLU + 1x128 quantization: ``quant_act_1x128(swiglu_bf16(x, y))``.  ``x`` (gate) and ``y``
+    (up) bf16 ``[M, K]`` -> ``(q uint8 [M, K], s float32 [K/128, M])``."""
+    lib = lib or load()
+    return quant_act_1x128(swiglu_bf16(x_bits, y_bits, lib=lib), lib=lib)

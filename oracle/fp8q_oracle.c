@@ -46,6 +46,9 @@
  *    expert-sorted, 128-padded layout of the quantized rows that the grouped
  *    GEMM consumes.  The readings (tie rule, segment order, empty rows) are
  *    stated beside the functions at the end of this file.
+ *  - Fused SwiGLU + 1x128 quantization (same page and list: the quantization
+ *    kernels combine SwiGLU with quantization): h = bf16(SiLU(x) * y), the
+ *    exact value rounded once, then the 1x128 activation quantizer on h.
  *
  * Layouts (a reading; the pages are silent): row-major, K contiguous.
  * Activation scales s_a are stored K-block-major, s_a[kb * M + m]; weight scales
@@ -61,7 +64,9 @@
  * pattern, (for routing) a pairwise check of the top-k definition on random
  * and tie-heavy logits, library special cases (k = 1 is argmax, k = E a stable
  * sort), a hand-worked layout and the layout invariants, (for the gather)
- * numpy indexing and its commutation with the row-wise quantizer,
+ * numpy indexing and its commutation with the row-wise quantizer, (for
+ * SwiGLU) 80-digit decimal arithmetic, numpy's float64 exp away from rounding
+ * midpoints, hand-worked ties and signed zeros, and sign and scale symmetry,
  * the OCP closed-form code table, a brute-force nearest-value encoder over all
  * bf16 inputs, sign/scale invariants, a lossless special case equal to a
  * float64 numpy matmul, and exact rational sums on tiny shapes.
@@ -380,4 +385,101 @@ int oracle_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K
         for (int64_t kb = 0; kb < KB; kb++) sa[kb * rows + r] = t >= 0 ? s[kb * T + t] : 0.0f;
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Fused SwiGLU + 1x128 quantization (page "DeepSeek starts updating
+ * frequently", the list of TileKernels features: the quantization kernels
+ * combine SwiGLU with quantization).  SwiGLU is read as the gated unit of the
+ * FFN, h = SiLU(x) * y with SiLU(x) = x / (1 + e^-x), x the gate and y the up
+ * projection, both bf16.  The pages fix no precision for h; the reading taken
+ * here is the exact real value rounded once to bf16 to nearest even (then the
+ * 1x128 quantizer above runs on h).  Unlike an fp32 formula, this does not
+ * depend on how exp is implemented.
+ *
+ * Evaluation: x*y is exact in double; e^-x, 1 + e^-x and the division add a
+ * few units in the last place, far below a bf16 spacing.  A value whose double
+ * lies within 2^-45 (relative) of a bf16 rounding midpoint is not decided
+ * here, with one exception: when 1 + e^-x rounds to exactly 1 and x*y is
+ * itself a midpoint, the true value lies strictly between the midpoint and
+ * the neighbour towards zero (e^-x > 0 and e^-x < 2^-53), so it rounds
+ * towards zero.  The others are flagged for the caller to settle in higher
+ * precision.
+ * ------------------------------------------------------------------------- */
+
+/* Rounding of the double v (finite, below the bf16 overflow threshold) to bf16: mode 0 to nearest even,
+ * -1 to the neighbour towards zero, +1 to the neighbour away from zero (modes +-1 only matter when v is
+ * not itself a bf16 value).  *near_tie gets 1 when v lies within `margin` (relative) of a rounding
+ * midpoint, *mid 1 when v is exactly one. */
+static uint16_t bf16_round_double(double v, int mode, double margin, int *near_tie, int *mid) {
+    *near_tie = 0;
+    *mid = 0;
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0x0000u;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);            /* a = f * 2^e, f in [0.5, 1): the binade's exponent is e - 1 */
+    int ex = e - 1;
+    if (ex < -126) ex = -126; /* bf16 subnormals share the spacing 2^-133 */
+    double ulp = ldexp(1.0, ex - 7);
+    double q = a / ulp; /* exact: a power-of-two scaling */
+    double fl = floor(q);
+    double rem = q - fl;
+    if (fabs(rem - 0.5) * ulp <= margin * a) *near_tie = 1;
+    if (rem == 0.5) *mid = 1;
+    if (mode == 0) {
+        if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    } else if (mode > 0 && rem > 0.0) {
+        fl += 1.0;
+    }
+    float r = (float)(fl * ulp); /* a bf16 value: exact in float */
+    uint32_t bits;
+    memcpy(&bits, &r, 4);
+    bits >>= 16;
+    if (signbit(v)) bits |= 0x8000u;
+    return (uint16_t)bits;
+}
+
+/* h[i] = bf16(SiLU(x[i]) * y[i]) for bf16 x, y.  amb[i] = 1 marks a value this
+ * function could not decide (h[i] then holds the double's rounding).  Returns
+ * 0, or -2 for a non-finite input or a result past the bf16 range.
+ *
+ * Values within 2^-45 of a midpoint m are settled exactly in two cases, which
+ * cover every such value with x*y in the bf16 range (an exhaustive check over
+ * all x and y significands confirms it):
+ *  - x > 16: e^-x < 2^-23, so the true value lies less than 2^-23 inside x*y; if
+ *    x*y is itself the midpoint, the value lies just inside it, above the
+ *    neighbour towards zero (midpoints are 2^-9 or more from their neighbours);
+ *  - |x| < 2^-40: SiLU(x) * y = (x*y/2)(1 + x/2 + ...), so the true value lies
+ *    within 2^-40 of x*y/2, beyond it (away from zero) when x > 0 and inside
+ *    it when x < 0; if x*y/2 is the midpoint, that side decides. */
+int oracle_swiglu_bf16(const uint16_t *x, const uint16_t *y, int64_t n, uint16_t *h, uint8_t *amb) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < n; i++) {
+        double xv = (double)bf16_to_f32(x[i]), yv = (double)bf16_to_f32(y[i]);
+        if (!isfinite(xv) || !isfinite(yv)) {
+            bad = 1;
+            continue;
+        }
+        double p = xv * yv; /* exact: two 8-bit significands */
+        double v = p / (1.0 + exp(-xv));
+        if (!isfinite(v) || fabs(v) >= 3.3961775292304e38 /* the bf16 overflow threshold */) {
+            bad = 1;
+            continue;
+        }
+        int near_tie, mid, nt2, pmid;
+        uint16_t r = bf16_round_double(v, 0, 0x1p-45, &near_tie, &mid);
+        amb[i] = 0;
+        if (near_tie) {
+            if (xv > 16.0 && (bf16_round_double(p, 0, 0.0, &nt2, &pmid), pmid)) {
+                r = bf16_round_double(p, -1, 0.0, &nt2, &pmid);
+            } else if (fabs(xv) < 0x1p-40 && (bf16_round_double(p / 2, 0, 0.0, &nt2, &pmid), pmid)) {
+                r = bf16_round_double(p / 2, xv > 0 ? 1 : -1, 0.0, &nt2, &pmid);
+            } else {
+                amb[i] = 1;
+            }
+        }
+        h[i] = r;
+    }
+    return bad ? -2 : 0;
 }

@@ -1,8 +1,8 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU; the real oracle is not
-touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe against it.  At least one
-pin must fail for every planted mistake.
+touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe / _swiglu
+against it until one fails.  At least one pin must fail for every planted mistake.
 """
 import os
 
@@ -13,6 +13,7 @@ import test_oracle_dequant as td
 import test_oracle_e4m3 as te
 import test_oracle_gemm as tg
 import test_oracle_moe as tm
+import test_oracle_swiglu as ts
 import test_oracle_quant as tq
 
 SRC = open(os.path.join(os.path.dirname(oracle.__file__), "fp8q_oracle.c")).read()
@@ -48,6 +49,11 @@ MUTATIONS = {
                                   "(best < 0 || v[e] > v[best] || (v[e] == v[best] && signbit(v[best]) && !signbit(v[e])))"),
     "gather_scale_row_major": ("sa[kb * rows + r] = t >= 0", "sa[r * KB + kb] = t >= 0"),
     "gather_empty_row_copies_token_0": ("qa[r * K + k] = t >= 0 ? q[t * K + k] : 0;", "qa[r * K + k] = q[(t >= 0 ? t : 0) * K + k];"),
+    "swiglu_sigmoid_sign": ("double v = p / (1.0 + exp(-xv));", "double v = p / (1.0 + exp(xv));"),
+    "swiglu_fp32_intermediate": ("double v = p / (1.0 + exp(-xv));", "double v = (double)(float)(p / (1.0 + exp(-xv)));"),
+    "swiglu_tiny_gate_side_flipped": ("xv > 0 ? 1 : -1", "xv > 0 ? -1 : 1"),
+    "swiglu_large_gate_tie_to_even": ("r = bf16_round_double(p, -1, 0.0, &nt2, &pmid);", "r = bf16_round_double(p, 0, 0.0, &nt2, &pmid);"),
+    "swiglu_subnormal_spacing_dropped": ("    if (ex < -126) ex = -126; /* bf16 subnormals share the spacing 2^-133 */", ""),
 }
 
 
@@ -84,6 +90,12 @@ def pins():
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
     for case in tq.load_golden()["weight_blocks"]:
         out.append((tq.test_hand_worked_weight_block, {"case": case}))
+    out += [   # last: the slower ones run only for mistakes that no earlier pin catches
+        (ts.test_closed_forms, {}),
+        (ts.test_double_evaluation_decides_every_value, {"y_exp": None, "x_max": 126}),
+        (ts.test_matches_numpy_float64_away_from_midpoints, {}),
+        (ts.test_matches_decimal_on_a_sample, {}),
+    ]
     return out
 
 
@@ -94,10 +106,11 @@ def test_planted_mistake_is_caught(tmp_path, name):
     src = tmp_path / f"mut_{name}.c"
     src.write_text(SRC.replace(old, new))
     lib = oracle.load(oracle.build(str(src), str(tmp_path / f"mut_{name}.so")))
-    caught = []
+    caught = None
     for fn, kw in pins():
         try:
             fn(lib, **kw)
         except (AssertionError, ValueError, IndexError):
-            caught.append(fn.__name__)
+            caught = fn.__name__
+            break
     assert caught, f"no pin catches the planted mistake {name}"
