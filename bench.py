@@ -44,8 +44,9 @@ DESCRIPTIONS = {
     "up": "dense FFN up-projection: A bf16 [4096,7168] ~N(0,1) with 72 (1%) outlier channels x20, W bf16 "
           "[18432,7168] ~N(0,0.02); 1x128 act quant + 128x128 weight quant + block-scaled FP8 GEMM -> bf16 "
           "[4096,18432]",
-    "down": "dense FFN down-projection: A = bf16(SiLU(x)*y) [4096,18432], W bf16 [7168,18432] ~N(0,0.02); "
-            "1x128 act quant + 128x128 weight quant + block-scaled FP8 GEMM -> bf16 [4096,7168]",
+    "down": "dense FFN down-projection: gate x, up y bf16 [4096,18432] ~N(0,1), W bf16 [7168,18432] ~N(0,0.02); "
+            "fused SwiGLU + 1x128 act quant of A = bf16(SiLU(x)*y) + 128x128 weight quant + block-scaled FP8 "
+            "GEMM -> bf16 [4096,7168]",
     "moe": "MoE layer: 8192 tokens x 7168 bf16 ~N(0,1), router logits [8192,64] ~N(0,1), expert W bf16 "
            "[64][2048,7168] ~N(0,0.02); 1x128 act quant of the tokens + top-8 routing + FP8 row gather into "
            "128-padded expert segments + 128x128 weight quant + grouped block-scaled FP8 GEMM -> bf16",
@@ -109,11 +110,17 @@ class Workload:
         if name == "moe":
             self._init_moe(d, bf16, dev)
             return
-        self.a = bf16(d["a"])
         self.qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
         self.sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
-        kernels = [("quant_act_1x128", lambda: fq.fp8q_quant_act_1x128(self.a, self.qa, self.sa),
-                    {"bytes": act_bytes(M, K)})]
+        if name == "down":   # the activation is SwiGLU(gate, up), quantized by the fused kernel
+            self.x, self.y = bf16(d["x"]), bf16(d["y"])
+            kernels = [("swiglu_quant_act_1x128",
+                        lambda: fq.fp8q_swiglu_quant_act_1x128(self.x, self.y, self.qa, self.sa),
+                        {"bytes": act_bytes(M, K) + 2 * M * K})]
+        else:
+            self.a = bf16(d["a"])
+            kernels = [("quant_act_1x128", lambda: fq.fp8q_quant_act_1x128(self.a, self.qa, self.sa),
+                        {"bytes": act_bytes(M, K)})]
         if name == "decode":
             wq = torch.from_numpy(d["wq"]).to(dev)
             self.qw_copies = [wq] + [wq.clone() for _ in range(3)]
@@ -230,8 +237,15 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
         w_bits, a_src = d["w"][e], d["tokens"][seg[seg >= 0]]
     elif wk.name == "decode":
         w_bits, a_src = None, d["a"]
+    elif wk.name == "down":
+        w_bits, a_src = d["w"], None   # rows of SiLU(x) * y, made below by the oracle inside the timing
     else:
         w_bits, a_src = d["w"], d["a"]
+
+    def act(r):
+        if a_src is not None:
+            return oracle.quant_act_1x128(a_src[:r], lib=lib)
+        return oracle.swiglu_quant_1x128(d["x"][:r], d["y"][:r], lib=lib)
     t0 = time.perf_counter()
     if w_bits is not None:
         qw, sw = oracle.quant_w_128x128(w_bits, lib=lib)
@@ -239,13 +253,14 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
         qw, sw = d["wq"], d["sw"]
     t_w = time.perf_counter() - t0
     # calibrate the GEMM rate on one row, then size the sample to about `target_s` seconds in total
-    qa, sa = oracle.quant_act_1x128(a_src[:1], lib=lib)
+    qa, sa = act(1)
     t1 = time.perf_counter()
     oracle.gemm_blockscaled(qa, sa, qw, sw, rows=[0], lib=lib)
     per_row = time.perf_counter() - t1
-    rows = int(max(1, min(a_src.shape[0], (target_s - t_w) / max(per_row, 1e-6))))
+    n_src = a_src.shape[0] if a_src is not None else d["x"].shape[0]
+    rows = int(max(1, min(n_src, (target_s - t_w) / max(per_row, 1e-6))))
     t2 = time.perf_counter()
-    qa, sa = oracle.quant_act_1x128(a_src[:rows], lib=lib)
+    qa, sa = act(rows)
     oracle.gemm_blockscaled(qa, sa, qw, sw, rows=np.arange(rows), lib=lib)
     t_rows = time.perf_counter() - t2
     total = t_w + t_rows
@@ -253,7 +268,8 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
     what = "expert 0's weights" if wk.name == "moe" else ("pre-quantized weights" if wk.name == "decode" else
                                                          "all weights")
     return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
-            "sample": f"{rows} token rows x all {N} outputs (K={K}): their 1x128 quantization, 128x128 "
+            "sample": f"{rows} token rows x all {N} outputs (K={K}): their "
+                      f"{'SwiGLU and ' if wk.name == 'down' else ''}1x128 quantization, 128x128 "
                       f"quantization of {what}, and the double-precision GEMM of those rows; {total:.1f} s"}
 
 

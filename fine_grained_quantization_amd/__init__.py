@@ -5,6 +5,8 @@ this package is its Python binding.  Entry points (same names as the C functions
 
   fp8q_quant_act_1x128(x)                      bf16 [M, K] -> (E4M3 [M, K], fp32 scales [K/128, M])
   fp8q_quant_w_128x128(w)                      bf16 [N, K] -> (E4M3 [N, K], fp32 scales [N/128, K/128])
+  fp8q_swiglu_quant_act_1x128(x, y)            bf16 gate, up [M, K] -> 1x128 quantization of bf16(SiLU(x) * y)
+  fp8q_swiglu_bf16(x, y)                       the bf16 intermediate SiLU(x) * y alone
   fp8q_gemm_blockscaled(qa, sa, qw, sw)        -> C = A W^T, bf16 or fp32 [M, N]
   fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets)   MoE experts, one segment of rows each
   fp8q_dequant_w_128x128(q, s)                 E4M3 [N, K] + fp32 [N/128, K/128] -> bf16 [N, K]
@@ -23,6 +25,8 @@ from ._binding import (  # noqa: F401
     fp8q_moe_route_topk,
     fp8q_quant_act_1x128,
     fp8q_quant_w_128x128,
+    fp8q_swiglu_bf16,
+    fp8q_swiglu_quant_act_1x128,
     load_library,
     status_string,
 )

@@ -35,12 +35,16 @@ def load_library(path: str = LIB_PATH):
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.fp8q_quant_act_1x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_quant_w_128x128.argtypes = [P, I64, I64, P, P, P]
+        lib.fp8q_swiglu_quant_act_1x128.argtypes = [P, P, I64, I64, I64, P, P, P]
+        lib.fp8q_swiglu_bf16.argtypes = [P, P, I64, I64, I64, P, P]
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
         lib.fp8q_moe_route_topk.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, P]
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
-        for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_gemm_blockscaled,
+        for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
+                  lib.fp8q_swiglu_bf16,
+                  lib.fp8q_gemm_blockscaled,
                   lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
                   lib.fp8q_moe_gather_fp8):
             f.restype = ctypes.c_int
@@ -108,6 +112,65 @@ def fp8q_quant_act_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torc
     _check(load_library().fp8q_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
            "fp8q_quant_act_1x128")
     return q, s
+
+
+def fp8q_swiglu_quant_act_1x128(x: torch.Tensor, y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                                s: torch.Tensor | None = None, stream=None):
+    """Fused SwiGLU + 1x128 quantization of h = bf16(SiLU(x) * y).  Either ``x`` (gate) and ``y`` (up) bf16
+    [M, K] with equal row strides (views are fine), or ``x`` alone as one [M, 2K] tensor whose halves are the
+    gate and the up projection -> ``(q uint8 [M, K], s float32 [K/128, M])``."""
+    _need_rows(x, "x")
+    if y is None:
+        M, K2 = x.shape
+        if K2 % 2:
+            raise ValueError("a fused gate/up tensor needs an even number of columns")
+        K = K2 // 2
+        ld = x.stride(0)
+        y = x[:, K:]
+        x = x[:, :K]
+    else:
+        _need_rows(y, "y")
+        if y.shape != x.shape or y.stride(0) != x.stride(0):
+            raise ValueError("x and y must have the same shape and row stride")
+        M, K = x.shape
+        ld = x.stride(0)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _need(q, "q", _FP8)
+    _need(s, "s", (torch.float32,))
+    if q.numel() != M * K or s.numel() != (K // 128) * M:
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_swiglu_quant_act_1x128(_ptr(x), _ptr(y), ld, M, K, _ptr(q), _ptr(s),
+                                                      _stream_ptr(stream)), "fp8q_swiglu_quant_act_1x128")
+    return q, s
+
+
+def fp8q_swiglu_bf16(x: torch.Tensor, y: torch.Tensor, h: torch.Tensor | None = None, stream=None):
+    """h = bf16(SiLU(x) * y) written out (the intermediate the fused quantizer keeps in registers).  ``x``,
+    ``y`` bf16 [M, K] with equal row strides -> ``h`` bf16 [M, K]."""
+    _need_rows(x, "x")
+    _need_rows(y, "y")
+    if y.shape != x.shape or y.stride(0) != x.stride(0):
+        raise ValueError("x and y must have the same shape and row stride")
+    M, K = x.shape
+    if h is None:
+        h = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _need(h, "h", _BF16)
+    if h.numel() != M * K:
+        raise ValueError("h has the wrong size")
+    _check(load_library().fp8q_swiglu_bf16(_ptr(x), _ptr(y), x.stride(0), M, K, _ptr(h), _stream_ptr(stream)),
+           "fp8q_swiglu_bf16")
+    return h
+
+
+def _need_rows(t, name):
+    """A bf16 [M, K] device view whose rows are contiguous (any row stride)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype not in _BF16 or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D bf16 device tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
 
 
 def fp8q_quant_w_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,

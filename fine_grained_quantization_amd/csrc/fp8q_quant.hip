@@ -60,6 +60,143 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
 }
 
 // ---------------------------------------------------------------------------------------------
+// Fused SwiGLU + 1x128 quantization (page "DeepSeek starts updating frequently", the TileKernels feature
+// list: quantization combined with SwiGLU).  h = SiLU(x) * y with SiLU(x) = x / (1 + e^-x), the exact value
+// rounded once to bf16 (nearest even), then quantized like the activations above; h never leaves registers.
+//
+// Per element: an fp32 value of x*y / (1 + e^-x) with a proven error bound (below); where its low 16 bits
+// are far enough from the bf16 rounding midpoint, its nearest-even bf16 is the correctly rounded one.  The
+// rest (a few in 10^4 for N(0,1) gates, plus zeros, tiny and non-finite intermediates) take a double path:
+// x*y is exact, the quotient within a few double ulps; two classes sit closer to a midpoint than that and are
+// settled by where the exact value must lie: gates above 16 with x*y itself a midpoint (the value lies just
+// inside it, towards zero) and gates below 2^-40 with x*y/2 a midpoint (the value lies beyond it for x > 0,
+// inside it for x < 0).  No other bf16 pair comes within 2^-45 of a midpoint.
+// ---------------------------------------------------------------------------------------------
+
+// Rounding of a finite double to bf16: mode 0 nearest even, -1 towards zero, +1 away from zero.  Bit 31 of
+// the result is set when v is exactly a midpoint between two bf16 values.
+constexpr uint32_t kMidFlag = 0x80000000u;
+
+__device__ __forceinline__ uint32_t bf16_round_f64(double v, int mode) {
+    if (v == 0.0) return __builtin_signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    int ex = ilogb(a);
+    if (ex < -126) ex = -126;  // bf16 subnormals share the spacing 2^-133
+    const double q = ldexp(a, 7 - ex);  // exact: a power-of-two scaling
+    double fl = floor(q);
+    const double rem = q - fl;
+    if (mode == 0) {
+        if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    } else if (mode > 0 && rem > 0.0) {
+        fl += 1.0;
+    }
+    const float r = (float)ldexp(fl, ex - 7);  // a bf16 value: exact in float
+    return (__float_as_uint(r) >> 16) | (__builtin_signbit(v) ? 0x8000u : 0u) | (rem == 0.5 ? kMidFlag : 0u);
+}
+
+__device__ __noinline__ uint32_t swiglu_bf16_f64(float xf, float yf) {
+    const double x = xf, p = x * (double)yf;  // exact
+    if (x > 16.0) {
+        const uint32_t r = bf16_round_f64(p, -1);
+        if (r & kMidFlag) return r & 0xFFFFu;
+    } else if (fabs(x) < 0x1p-40 && x != 0.0) {
+        const uint32_t r = bf16_round_f64(p * 0.5, x > 0.0 ? 1 : -1);
+        if (r & kMidFlag) return r & 0xFFFFu;
+    }
+    return bf16_round_f64(p / (1.0 + exp(-x)), 0) & 0xFFFFu;
+}
+
+// bf16 bits of SiLU(x) * y for the bf16 pattern pairs in the low halves of xb, yb.  Fast path in fp32:
+// e = exp2(fl(-x log2 e)) with the hardware v_exp_f32.  Rounding -x log2 e shifts the exponent by at most
+// |x| 2^-24 relative, so e carries at most |x| 2^-24 + 2^-23 relative error; 1 + e, v_rcp_f32 and the final
+// product add at most 2^-24 + 2^-23 + 2^-24.  x*y is exact while the result is a normal number (|h| >= 2^-120
+// implies |x*y| >= 2^-120), so h = (x*y) rcp(1 + e) is within |x| + 6 fp32 units in the last place of the
+// exact value, and its nearest-even bf16 is the correctly rounded one when its low 16 bits are more than twice
+// that from the midpoint 0x8000.
+__device__ __forceinline__ uint32_t swiglu_bf16(uint32_t xb, uint32_t yb) {
+    const float x = __uint_as_float(xb << 16), y = __uint_as_float(yb << 16);
+    const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896340736f);
+    const float h = (x * y) * __builtin_amdgcn_rcpf(1.0f + e);
+    const uint32_t bits = __float_as_uint(h);
+    const float off = fabsf((float)((int)(bits & 0xFFFFu) - 0x8000));
+    const bool fast = fabsf(h) >= 0x1p-120f && fabsf(h) <= 0x1p126f && off > 16.0f + 2.0f * fabsf(x);
+    if (fast) return (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+    return swiglu_bf16_f64(x, y);
+}
+
+__device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t xd, uint32_t yd) {
+    return swiglu_bf16(xd & 0xFFFFu, yd & 0xFFFFu) | (swiglu_bf16(xd >> 16, yd >> 16) << 16);
+}
+
+// Same layout as quant_act_1x128_kernel; x and y rows are ld elements apart (so the gate and up halves of
+// one [M, 2K] projection can be passed as two views).
+__global__ __launch_bounds__(256) void swiglu_quant_act_1x128_kernel(const uint16_t *__restrict__ x,
+                                                                     const uint16_t *__restrict__ y, int64_t ld,
+                                                                     int64_t M, int64_t K, uint8_t *__restrict__ q,
+                                                                     float *__restrict__ s) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t KB = K >> 7;
+    const int64_t KQ = (KB + 3) >> 2;
+    const int64_t kq = (int64_t)blockIdx.x % KQ;
+    const int64_t row0 = ((int64_t)blockIdx.x / KQ) * 16 + wave * 4;
+    const int64_t kb = kq * 4 + (lane >> 4);
+    const int i = lane & 15;
+    const bool kb_ok = kb < KB;
+    const int64_t kbr = kb_ok ? kb : KB - 1;
+
+    u32x4 vx[4], vy[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t m = row0 + j;
+        const int64_t mr = m < M ? m : M - 1;
+        vx[j] = load_stream16(x + mr * ld + kbr * 128 + i * 8);
+        vy[j] = load_stream16(y + mr * ld + kbr * 128 + i * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        u32x4 h;
+        h.x = swiglu_bf16x2(vx[j].x, vy[j].x);
+        h.y = swiglu_bf16x2(vx[j].y, vy[j].y);
+        h.z = swiglu_bf16x2(vx[j].z, vy[j].z);
+        h.w = swiglu_bf16x2(vx[j].w, vy[j].w);
+        float amax = 0.0f;
+        amax = absmax2(amax, h.x);
+        amax = absmax2(amax, h.y);
+        amax = absmax2(amax, h.z);
+        amax = absmax2(amax, h.w);
+        amax = row16_max(amax);
+        const float sc = group_scale(amax);
+        const double inv = scale_reciprocal(sc);
+        const int64_t m = row0 + j;
+        if (m < M && kb_ok) {
+            uint2 o;
+            o.x = quant4(h.x, h.y, inv);
+            o.y = quant4(h.z, h.w, inv);
+            *reinterpret_cast<uint2 *>(q + m * K + kb * 128 + i * 8) = o;
+            if (i == 0) s[kb * M + m] = sc;
+        }
+    }
+}
+
+// h = bf16(SiLU(x) * y) alone (the intermediate the fused kernel quantizes), 8 elements per thread.
+__global__ __launch_bounds__(256) void swiglu_bf16_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ y, int64_t ld, int64_t M,
+                                                          int64_t K, uint16_t *__restrict__ h) {
+    const int64_t per_row = K >> 3;
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= M * per_row) return;
+    const int64_t m = u / per_row, k = (u - m * per_row) * 8;
+    const u32x4 vx = load_stream16(x + m * ld + k), vy = load_stream16(y + m * ld + k);
+    u32x4 o;
+    o.x = swiglu_bf16x2(vx.x, vy.x);
+    o.y = swiglu_bf16x2(vx.y, vy.y);
+    o.z = swiglu_bf16x2(vx.z, vy.z);
+    o.w = swiglu_bf16x2(vx.w, vy.w);
+    *reinterpret_cast<u32x4 *>(h + m * K + k) = o;
+}
+
+// ---------------------------------------------------------------------------------------------
 // 128x128 weights.  One workgroup (256 threads) per block.  In load i (0..7) thread t reads the
 // 16-byte chunk (t % 16) of block row (t / 16 + 16 i): 16 threads cover a 256-byte row, one
 // instruction covers 16 rows.  The block max is a wave reduction plus a 4-entry LDS exchange.
@@ -159,6 +296,21 @@ hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8
                                   hipStream_t stream) {
     const int64_t blocks = (N / 128) * (K / 128);  // 1-D grid: K-block fastest
     quant_w_128x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant_act_1x128(const uint16_t *x, const uint16_t *y, int64_t ld, int64_t M, int64_t K,
+                                         uint8_t *q, float *s, hipStream_t stream) {
+    const int64_t KQ = (K / 128 + 3) / 4;
+    const int64_t blocks = (M + 15) / 16 * KQ;
+    swiglu_quant_act_1x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, y, ld, M, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bf16(const uint16_t *x, const uint16_t *y, int64_t ld, int64_t M, int64_t K, uint16_t *h,
+                              hipStream_t stream) {
+    const int64_t blocks = (M * (K / 8) + 255) / 256;
+    swiglu_bf16_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, y, ld, M, K, h);
     return hipGetLastError();
 }
 

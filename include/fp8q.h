@@ -71,6 +71,31 @@ typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 } fp8q_out_dtype;
  * Requires M >= 0, K >= 0, K % 128 == 0. */
 int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* Fused SwiGLU + 1x128 activation quantization (page "DeepSeek starts updating
+ * frequently", the list of TileKernels features: the quantization kernels
+ * combine SwiGLU with quantization).  The pages do not give the arithmetic;
+ * this library reads SwiGLU as the FFN's gated unit and fixes one rounding:
+ *   h[m,k] = bf16_RNE( SiLU(x[m,k]) * y[m,k] ),  SiLU(x) = x / (1 + e^-x),
+ * the exact value rounded once to bf16 (so the result does not depend on how
+ * exp is implemented), then q, s = the 1x128 quantization of h exactly as
+ * fp8q_quant_act_1x128 computes it.  h is never written to memory.
+ *   x  : bf16 gate [M, K], rows ld elements apart   (input)
+ *   y  : bf16 up   [M, K], rows ld elements apart   (input; x and y may be the
+ *        two halves of one [M, 2K] tensor: y = x + K, ld = 2K)
+ *   q  : E4M3 [M, K]            (output)
+ *   s  : fp32 [K/128][M]        (output)
+ * Requires M >= 0, K % 128 == 0, ld >= K, ld % 8 == 0, 16-byte aligned
+ * pointers.  Finite inputs whose h stays in the bf16 range are a
+ * precondition. */
+int fp8q_swiglu_quant_act_1x128(const uint16_t *x, const uint16_t *y, int64_t ld, int64_t M, int64_t K, uint8_t *q,
+                                float *s, void *stream);
+
+/* The SwiGLU intermediate alone, h = bf16_RNE(SiLU(x) * y) as above, written
+ * out (the value fp8q_swiglu_quant_act_1x128 quantizes without storing it):
+ *   x, y : bf16 [M, K], rows ld elements apart (inputs);  h : bf16 [M, K] (output)
+ * Requires M >= 0, K % 8 == 0, ld >= K, ld % 8 == 0, 16-byte aligned pointers. */
+int fp8q_swiglu_bf16(const uint16_t *x, const uint16_t *y, int64_t ld, int64_t M, int64_t K, uint16_t *h, void *stream);
+
 /* 128x128 weight quantization (the Figure 7 (a) passage: per 128 input
  * channels per 128 output channels).
  *   w  : bf16 [N, K]            (input; an expert stack [E][N', K] is passed as N = E * N')

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("fp8q_quant_act_1x128", "fp8q_quant_w_128x128", "fp8q_gemm_blockscaled",
               "fp8q_grouped_gemm_blockscaled", "fp8q_dequant_w_128x128", "fp8q_moe_route_capacity",
               "fp8q_moe_route_workspace_bytes", "fp8q_moe_route_topk", "fp8q_moe_gather_fp8",
+              "fp8q_swiglu_quant_act_1x128", "fp8q_swiglu_bf16",
               "fp8q_status_string", "fp8q_version"):
         assert n in names
 
@@ -84,6 +85,19 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_dequant_w_128x128(A, None, 128, 128, B, None) == -1
     assert lib.fp8q_dequant_w_128x128(A, B, 128, 128, MIS, None) == -3
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, MIS, 0, 4, 128, 128, None) == -3
+    # fused SwiGLU + quantization, and the intermediate alone
+    sq, sw = lib.fp8q_swiglu_quant_act_1x128, lib.fp8q_swiglu_bf16
+    sq.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 3
+    sw.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2
+    assert sq(A, B, 100, 4, 100, B, B, None) == -2          # K not a multiple of 128
+    assert sq(A, B, 100, 4, 128, B, B, None) == -2          # ld < K
+    assert sq(A, B, 260, 4, 256, B, B, None) == -2          # ld not a multiple of 8
+    assert sq(None, None, 256, 0, 256, None, None, None) == 0
+    assert sq(A, None, 256, 4, 256, B, B, None) == -1
+    assert sq(A, MIS, 256, 4, 256, B, B, None) == -3
+    assert sw(A, B, 12, 4, 12, B, None) == -2                # K not a multiple of 8
+    assert sw(A, B, 16, 4, 16, None, None) == -1
+    assert sw(MIS, B, 16, 4, 16, B, None) == -3
 
 
 def test_moe_routing_sizes_and_validation(lib):

@@ -121,6 +121,8 @@ def sample_rows(M, n, seed):
 def test_full_size_dense_sampled(name, out):
     """Full-size FFN projections; every output column of sampled rows and every row of sampled columns."""
     d = wl.dense_up() if name == "up" else wl.dense_down()
+    if name == "down":   # A = bf16(SiLU(x) * y), from the oracle
+        d["a"] = oracle.swiglu_bf16(d["x"], d["y"])
     say(f"gemm: full {name} {d['M']}x{d['N']}x{d['K']} out={out}")
     c = gemm_out_to_f64(gpu_path(d["a"], d["w"], out))
     rows = sample_rows(d["M"], 16, 1)

@@ -116,6 +116,8 @@ def test_act_every_x_for_amax(amax_bits):
 def test_act_full_workloads(name):
     d = {"up": lambda: wl.dense_up(N=128), "down": lambda: wl.dense_down(N=128),
          "decode": lambda: wl.decode(N=128)}[name]()
+    if name == "down":   # A = bf16(SiLU(x) * y), from the oracle
+        d["a"] = oracle.swiglu_bf16(d["x"], d["y"])
     say(f"act quant: {name} A {d['a'].shape}")
     assert_same(*gpu_act(d["a"]), *oracle.quant_act_1x128(d["a"]), name)
 

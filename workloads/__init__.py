@@ -19,7 +19,8 @@ deepinsightai.io page):
 
   tiny    A [128, 512] ~ N(0,1), 4 channels x50; W [256, 512] ~ N(0, 0.02)       seed 0
   up      A [4096, 7168] ~ N(0,1), 72 (1%) channels x20; W [18432, 7168]         seed 1
-  down    A = bf16(SiLU(x) * y) [4096, 18432], x, y ~ N(0,1); W [7168, 18432]    seed 2
+  down    gate x, up y bf16 [4096, 18432] ~ N(0,1) (A = bf16(SiLU(x) * y) is the
+          method's fused SwiGLU step); W [7168, 18432] ~ N(0, 0.02)               seed 2
   moe     8192 tokens x 7168 ~ N(0,1); router logits [8192, 64] ~ N(0,1) (routed
           top-8, segments padded to 128 rows); W [64][2048, 7168] ~ N(0, 0.02)   seed 3
   decode  A [64, 7168] ~ N(0,1); W pre-quantized: E4M3 codes uniform over the 254
@@ -81,18 +82,10 @@ def activations_with_outliers(seed, M, K, n_outliers, factor, tid_a=T_A, tid_o=T
     return bf16_bits(a), ch
 
 
-def swiglu_activations(seed, M, K):
-    """A = bf16(fl32(SiLU(x) * y)), x, y ~ N(0,1) float32 (the down-projection input)."""
-    out = np.empty((M, K), dtype=np.uint16)
-    gx, gy = rng(seed, T_X), rng(seed, T_Y)
-    step = max(1, (1 << 25) // K)
-    for r0 in range(0, M, step):
-        r1 = min(M, r0 + step)
-        x = gx.standard_normal((r1 - r0, K), dtype=np.float32)
-        y = gy.standard_normal((r1 - r0, K), dtype=np.float32)
-        silu = x / (np.float32(1.0) + np.exp(-x))
-        out[r0:r1] = bf16_bits(silu * y)
-    return out
+def gate_up(seed, M, K):
+    """The FFN's gate x and up projection y in bf16, x, y ~ N(0,1), independent streams.  Their SwiGLU,
+    bf16(SiLU(x) * y), is the down projection's input; computing it is a step of the method."""
+    return normal_bf16(seed, T_X, (M, K)), normal_bf16(seed, T_Y, (M, K))
 
 
 def finite_e4m3_codes(seed, tid, shape):
@@ -127,9 +120,9 @@ def dense_up(M=4096, N=18432, K=7168):
 
 def dense_down(M=4096, N=7168, K=18432):
     s = SEEDS["down"]
-    a = swiglu_activations(s, M, K)
+    x, y = gate_up(s, M, K)
     w = normal_bf16(s, T_W, (N, K), 0.02)
-    return {"name": "down", "a": a, "w": w, "M": M, "N": N, "K": K}
+    return {"name": "down", "x": x, "y": y, "w": w, "M": M, "N": N, "K": K}
 
 
 def moe(T=8192, K=7168, E=64, k=8, N=2048, with_weights=True):
