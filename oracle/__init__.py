@@ -144,6 +144,18 @@ def quant_act_1x128(x_bits, lib=None):
     return q, s
 
 
+def quant_act_backward_copy(x_bits, lib=None):
+    """The FP8 copy of a Linear input that the backward pass contracts over tokens (the weight gradient
+    dW = dY^T X; page "The Definitive Information To Deepseek", the passage on caching the Linear's input in
+    FP8 for backward).  Reading: the 1x128 quantization of x^T, i.e. one scale per channel and 128 tokens,
+    from the same bf16 x as the forward copy.  ``x [M, K]`` with M a multiple of 128 ->
+    ``(q_t uint8 [K, M], s_t float32 [M/128, K])``: q_t[k, m] = E4M3(fl32(x[m, k] / s_t[m/128, k]))."""
+    x = _c(x_bits, np.uint16)
+    if x.shape[0] % 128:
+        raise ValueError("quant_act_backward_copy: M must be a multiple of 128")
+    return quant_act_1x128(np.ascontiguousarray(x.T), lib=lib)
+
+
 def quant_w_128x128(w_bits, lib=None):
     """128x128 weight quantization of bf16 ``w [N, K]`` (or ``[E, N, K]``, one block grid per expert).
 
