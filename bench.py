@@ -55,8 +55,12 @@ DESCRIPTIONS = {
     "tiny": "tiny: A bf16 [128,512] with 4 outlier channels x50, W bf16 [256,512]; full path -> bf16 [128,256]",
     "dequant": "FP8 -> BF16 weight conversion with 128x128 scales: E4M3 [18432,7168] (uniform finite codes), "
                "scales [144,56] ~U(1e-4,1e-2) -> bf16 [18432,7168]",
+    "dual": "forward and backward FP8 copies of the up projection's input: A bf16 [4096,7168] ~N(0,1) with 72 "
+            "outlier channels x20 -> 1x128 codes [4096,7168] + codes of A^T [7168,4096] (per channel, 128 tokens)",
 }
 DEQUANT_METRIC = "FP8 -> BF16 128x128 block dequantization GB/s (% HBM peak)"
+DUAL_METRIC = "one-pass forward (1x128) + backward (1x128 of x^T) FP8 copies of a Linear input GB/s (% HBM peak)"
+BANDWIDTH_METRICS = {"dequant": DEQUANT_METRIC, "dual": DUAL_METRIC}
 
 
 def log(msg):
@@ -97,6 +101,13 @@ class Workload:
         M, N, K = d["M"], d["N"], d["K"]
         self.M, self.N, self.K = M, N, K
         self.step_count = 0
+        if name == "dual":
+            self.a = bf16(d["a"])
+            self.flops = 0.0
+            self.bytes = 4 * M * K + 4 * (K // 128) * M + 4 * (M // 128) * K
+            self.kernels = [("quant_act_dual", lambda: fq.fp8q_quant_act_dual(self.a), {"bytes": self.bytes})]
+            torch.cuda.synchronize()
+            return
         if name == "dequant":
             self.qw = torch.from_numpy(d["wq"]).to(dev)
             self.sw = torch.from_numpy(d["sw"]).to(dev)
@@ -218,6 +229,20 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
     d = wk.host
     N, K = wk.N, wk.K
     lib = oracle.load()
+    if wk.name == "dual":
+        # calibrate on one 128-token block, then about target_s seconds' worth of blocks
+        t0 = time.perf_counter()
+        oracle.quant_act_1x128(d["a"][:128], lib=lib)
+        oracle.quant_act_backward_copy(d["a"][:128], lib=lib)
+        per = time.perf_counter() - t0
+        nb = int(max(1, min(wk.M // 128, target_s / max(per, 1e-6))))
+        t1 = time.perf_counter()
+        oracle.quant_act_1x128(d["a"][:128 * nb], lib=lib)
+        oracle.quant_act_backward_copy(d["a"][:128 * nb], lib=lib)
+        t = time.perf_counter() - t1
+        byts = wk.bytes * nb * 128 / wk.M
+        return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+                "sample": f"{128 * nb} of the {wk.M} tokens (K={K}), both copies; {t:.1f} s"}
     if wk.name == "dequant":
         # calibrate on one 128-row block row, then convert about target_s seconds' worth of block rows
         t0 = time.perf_counter()
@@ -458,7 +483,7 @@ def main():
     gname, _, gwork = wk.kernels[-1]
     g = kernels[gname]
     traffic = profiled_traffic(gname, args.workload)
-    if args.workload == "dequant":
+    if args.workload in BANDWIDTH_METRICS:
         roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
     elif args.workload == "decode":
@@ -469,9 +494,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
     roof["algorithmic_bytes"] = int(gwork["bytes"])
 
-    dq = args.workload == "dequant"
+    dq = args.workload in BANDWIDTH_METRICS
     out = {
-        "metric": DEQUANT_METRIC if dq else METRIC,
+        "metric": BANDWIDTH_METRICS[args.workload] if dq else METRIC,
         "value": round(wk.bytes / (ms_step * 1e-3) / 1e9, 1) if dq else round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "GB/s" if dq else "TFLOP/s",
         "n_gpus": 1,
@@ -482,7 +507,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 -> bf16" if dq else "fp8_e4m3",
+        "dtype": {"dequant": "fp8_e4m3 -> bf16", "dual": "bf16 -> fp8_e4m3"}.get(args.workload, "fp8_e4m3"),
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,
                    "K": wk.K, "out": "bf16", "parallelism": "single GPU"},

@@ -37,13 +37,14 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_quant_w_128x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_swiglu_quant_act_1x128.argtypes = [P, P, I64, I64, I64, P, P, P]
         lib.fp8q_swiglu_bf16.argtypes = [P, P, I64, I64, I64, P, P]
+        lib.fp8q_quant_act_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
         lib.fp8q_moe_route_topk.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, P]
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
-                  lib.fp8q_swiglu_bf16,
+                  lib.fp8q_swiglu_bf16, lib.fp8q_quant_act_dual,
                   lib.fp8q_gemm_blockscaled,
                   lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
                   lib.fp8q_moe_gather_fp8):
@@ -112,6 +113,22 @@ def fp8q_quant_act_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torc
     _check(load_library().fp8q_quant_act_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
            "fp8q_quant_act_1x128")
     return q, s
+
+
+def fp8q_quant_act_dual(x: torch.Tensor, stream=None):
+    """Forward and backward FP8 copies of a Linear input in one pass.  ``x`` bf16 [M, K] (M, K multiples of
+    128) -> ``(q uint8 [M, K], s float32 [K/128, M], qt uint8 [K, M], st float32 [M/128, K])``: the 1x128
+    quantization of x and of x^T (per channel, per 128 tokens)."""
+    _need(x, "x", _BF16, 2)
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    qt = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    st = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+    _check(load_library().fp8q_quant_act_dual(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st),
+                                              _stream_ptr(stream)), "fp8q_quant_act_dual")
+    return q, s, qt, st
 
 
 def fp8q_swiglu_quant_act_1x128(x: torch.Tensor, y: torch.Tensor | None = None, q: torch.Tensor | None = None,

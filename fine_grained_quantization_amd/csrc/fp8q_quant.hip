@@ -60,6 +60,87 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
 }
 
 // ---------------------------------------------------------------------------------------------
+// Forward and backward FP8 copies of a Linear input in one pass (page "The Definitive Information To
+// Deepseek", the passage on caching the Linear's input in FP8 for the backward pass).  The backward pass
+// contracts the input over tokens (the weight gradient dW = dY^T x), so its copy is the 1x128 quantization
+// of x^T: one scale per channel and 128 tokens, stored channel-major.  A workgroup (256 threads) owns 128
+// tokens x 128 channels; thread t holds 8 consecutive tokens (8 (t / 16) ...) x 8 consecutive channels
+// (chunk t % 16), 8 loads of 16 bytes (a wave's load instruction covers 4 rows x 256 bytes).
+//  - forward copy: a token's 128 channels lie in the 16 lanes of one DPP row (8 row maxima per thread);
+//  - backward copy: a channel's 128 tokens lie in 16 threads spread over the 4 waves; their maxima over
+//    8 rows go through LDS, and each thread stores its 8 tokens' codes of each of its channels (8 bytes).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_at(const u32x4 &v, int c) {
+    const uint32_t d = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
+    return (c & 1) ? bf16_hi(d) : bf16_lo(d);
+}
+
+__global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                             uint8_t *__restrict__ q, float *__restrict__ s,
+                                                             uint8_t *__restrict__ qt, float *__restrict__ st) {
+    __shared__ float colmax[16][128];
+    __shared__ float colscale[128];
+    const int t = threadIdx.x;
+    const int64_t KB = K >> 7;
+    const int64_t kb = (int64_t)blockIdx.x % KB;
+    const int64_t mb = (int64_t)blockIdx.x / KB;
+    const int chunk = t & 15, g = t >> 4;
+    const int64_t m0 = mb * 128 + g * 8;
+    const int64_t c0 = kb * 128 + chunk * 8;
+
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = load_stream16(x + (m0 + j) * K + c0);
+
+    // forward: per token, 128 channels
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        float amax = 0.0f;
+        amax = absmax2(amax, v[j].x);
+        amax = absmax2(amax, v[j].y);
+        amax = absmax2(amax, v[j].z);
+        amax = absmax2(amax, v[j].w);
+        amax = row16_max(amax);
+        const float sc = group_scale(amax);
+        const double inv = scale_reciprocal(sc);
+        uint2 o;
+        o.x = quant4(v[j].x, v[j].y, inv);
+        o.y = quant4(v[j].z, v[j].w, inv);
+        *reinterpret_cast<uint2 *>(q + (m0 + j) * K + c0) = o;
+        if (chunk == 0) s[kb * M + m0 + j] = sc;
+    }
+
+    // backward: per channel, 128 tokens
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        float cm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) cm = fmaxf(cm, fabsf(bf16_at(v[j], c)));
+        colmax[g][chunk * 8 + c] = cm;
+    }
+    __syncthreads();
+    if (t < 128) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, colmax[i][t]);
+        const float sc = group_scale(amax);
+        colscale[t] = sc;
+        st[mb * K + kb * 128 + t] = sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        const double inv = scale_reciprocal(colscale[chunk * 8 + c]);
+        uint2 o;
+        o.x = encode4(quotient(bf16_at(v[0], c), inv), quotient(bf16_at(v[1], c), inv),
+                      quotient(bf16_at(v[2], c), inv), quotient(bf16_at(v[3], c), inv));
+        o.y = encode4(quotient(bf16_at(v[4], c), inv), quotient(bf16_at(v[5], c), inv),
+                      quotient(bf16_at(v[6], c), inv), quotient(bf16_at(v[7], c), inv));
+        *reinterpret_cast<uint2 *>(qt + (c0 + c) * M + m0) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Fused SwiGLU + 1x128 quantization (page "DeepSeek starts updating frequently", the TileKernels feature
 // list: quantization combined with SwiGLU).  h = SiLU(x) * y with SiLU(x) = x / (1 + e^-x), the exact value
 // rounded once to bf16 (nearest even), then quantized like the activations above; h never leaves registers.
@@ -304,6 +385,13 @@ hipError_t launch_swiglu_quant_act_1x128(const uint16_t *x, const uint16_t *y, i
     const int64_t KQ = (K / 128 + 3) / 4;
     const int64_t blocks = (M + 15) / 16 * KQ;
     swiglu_quant_act_1x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, y, ld, M, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
+                                 float *st, hipStream_t stream) {
+    const int64_t blocks = (M / 128) * (K / 128);
+    quant_act_dual_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s, qt, st);
     return hipGetLastError();
 }
 

@@ -71,6 +71,20 @@ typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 } fp8q_out_dtype;
  * Requires M >= 0, K >= 0, K % 128 == 0. */
 int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* Forward and backward FP8 copies of a Linear input in one pass (the passage
+ * on caching the Linear's input in FP8 for the backward pass).  The backward
+ * pass contracts the input over tokens (dW = dY^T x), so its FP8 copy needs
+ * groups along tokens; this library reads it as the 1x128 quantization of x^T
+ * (one scale per channel and 128 tokens), made from the same bf16 x:
+ *   x  : bf16 [M, K]            (input)
+ *   q  : E4M3 [M, K], s : fp32 [K/128][M]     (output: exactly fp8q_quant_act_1x128)
+ *   qt : E4M3 [K, M] (channel-major), st : fp32 [M/128][K]   (output)
+ *   qt[k,m] = E4M3_RNE_saturating(fl32(x[m,k] / st[m/128][k])),
+ *   st[mb][k] = fl32(max_{m in block mb} |x[m,k]| / 448).
+ * Requires M % 128 == 0, K % 128 == 0, 16-byte aligned pointers. */
+int fp8q_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt, float *st,
+                        void *stream);
+
 /* Fused SwiGLU + 1x128 activation quantization (page "DeepSeek starts updating
  * frequently", the list of TileKernels features: the quantization kernels
  * combine SwiGLU with quantization).  The pages do not give the arithmetic;

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("fp8q_quant_act_1x128", "fp8q_quant_w_128x128", "fp8q_gemm_blockscaled",
               "fp8q_grouped_gemm_blockscaled", "fp8q_dequant_w_128x128", "fp8q_moe_route_capacity",
               "fp8q_moe_route_workspace_bytes", "fp8q_moe_route_topk", "fp8q_moe_gather_fp8",
-              "fp8q_swiglu_quant_act_1x128", "fp8q_swiglu_bf16",
+              "fp8q_swiglu_quant_act_1x128", "fp8q_swiglu_bf16", "fp8q_quant_act_dual",
               "fp8q_status_string", "fp8q_version"):
         assert n in names
 
@@ -85,6 +85,14 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_dequant_w_128x128(A, None, 128, 128, B, None) == -1
     assert lib.fp8q_dequant_w_128x128(A, B, 128, 128, MIS, None) == -3
     assert lib.fp8q_gemm_blockscaled(A, A, A, A, MIS, 0, 4, 128, 128, None) == -3
+    # forward and backward copies in one pass: M and K multiples of 128
+    dual = lib.fp8q_quant_act_dual
+    dual.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5
+    assert dual(A, 100, 128, B, B, B, B, None) == -2
+    assert dual(A, 128, 100, B, B, B, B, None) == -2
+    assert dual(None, 0, 128, None, None, None, None, None) == 0
+    assert dual(A, 128, 128, B, B, None, B, None) == -1
+    assert dual(A, 128, 128, B, B, MIS, B, None) == -3
     # fused SwiGLU + quantization, and the intermediate alone
     sq, sw = lib.fp8q_swiglu_quant_act_1x128, lib.fp8q_swiglu_bf16
     sq.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 3

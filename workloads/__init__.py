@@ -152,4 +152,13 @@ def dequant(N=18432, K=7168):
     return {"name": "dequant", "wq": wq, "sw": sw, "M": 0, "N": N, "K": K}
 
 
-WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant}
+def dual(M=4096, K=7168):
+    """The up projection's input (same recipe and seed as the up workload's A), for the one-pass forward and
+    backward FP8 copies."""
+    s = SEEDS["up"]
+    a, ch = activations_with_outliers(s, M, K, int(round(0.01 * K)), 20.0)
+    return {"name": "dual", "a": a, "outlier_channels": ch, "M": M, "N": 0, "K": K}
+
+
+WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant,
+             "dual": dual}
