@@ -77,6 +77,16 @@ def load(path: str | None = None):
         lib.oracle_moe_gather_fp8.restype = ctypes.c_int
         lib.oracle_swiglu_bf16.argtypes = [P, P, I64, P, P]
         lib.oracle_swiglu_bf16.restype = ctypes.c_int
+        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_decode.restype = ctypes.c_double
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_e2m1_encode_array.argtypes = [P, I64, P]
+        lib.oracle_e2m1_encode_array.restype = None
+        lib.oracle_quant_act_fp4_1x128.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_act_fp4_1x128.restype = ctypes.c_int
+        lib.oracle_quant_w_fp4_128x128.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_w_fp4_128x128.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -391,3 +401,46 @@ def swiglu_quant_1x128(x_bits, y_bits, lib=None):
     (up) bf16 ``[M, K]`` -> ``(q uint8 [M, K], s float32 [K/128, M])``."""
     lib = lib or load()
     return quant_act_1x128(swiglu_bf16(x_bits, y_bits, lib=lib), lib=lib)
+
+
+# ---------------------------------------------------------------------------
+# FP4 (OCP E2M1) quantization in the FP8 groupings
+# ---------------------------------------------------------------------------
+
+def e2m1_decode(codes, lib=None) -> np.ndarray:
+    """Values of 4-bit E2M1 codes (0..15)."""
+    lib = lib or load()
+    c = np.asarray(codes, np.uint8)
+    return np.array([lib.oracle_e2m1_decode(int(v)) for v in c.reshape(-1)]).reshape(c.shape)
+
+
+def e2m1_encode(values, lib=None) -> np.ndarray:
+    """Nearest E2M1 codes (ties to the even code, saturating at +-6) of float32 values."""
+    lib = lib or load()
+    v = _c(values, np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib.oracle_e2m1_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def quant_act_fp4_1x128(x_bits, lib=None):
+    """1x128 FP4 activation quantization: ``x [M, K]`` bf16 -> ``(q uint8 [M, K/2], s float32 [K/128, M])``,
+    two codes a byte (element 2i in the low nibble), scale = fl32(amax / 6)."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K // 2), dtype=np.uint8)
+    s = np.empty((K // 128, M), dtype=np.float32)
+    _check(lib.oracle_quant_act_fp4_1x128(_ptr(x), M, K, _ptr(q), _ptr(s)), "quant_act_fp4_1x128")
+    return q, s
+
+
+def quant_w_fp4_128x128(w_bits, lib=None):
+    """128x128 FP4 weight quantization: ``w [N, K]`` bf16 -> ``(q uint8 [N, K/2], s float32 [N/128, K/128])``."""
+    lib = lib or load()
+    w = _c(w_bits, np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K // 2), dtype=np.uint8)
+    s = np.empty((N // 128, K // 128), dtype=np.float32)
+    _check(lib.oracle_quant_w_fp4_128x128(_ptr(w), N, K, _ptr(q), _ptr(s)), "quant_w_fp4_128x128")
+    return q, s

@@ -46,6 +46,9 @@
  *    expert-sorted, 128-padded layout of the quantized rows that the grouped
  *    GEMM consumes.  The readings (tie rule, segment order, empty rows) are
  *    stated beside the functions at the end of this file.
+ *  - FP4 (E2M1) quantization in the FP8 groupings (same page and list: the
+ *    quantization kernels convert to FP8, FP4 or E5M6); readings beside the
+ *    functions.
  *  - Fused SwiGLU + 1x128 quantization (same page and list: the quantization
  *    kernels combine SwiGLU with quantization): h = bf16(SiLU(x) * y), the
  *    exact value rounded once, then the 1x128 activation quantizer on h.
@@ -480,6 +483,111 @@ int oracle_swiglu_bf16(const uint16_t *x, const uint16_t *y, int64_t n, uint16_t
             }
         }
         h[i] = r;
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * FP4 quantization (page "DeepSeek starts updating frequently", the list of
+ * TileKernels features: the quantization kernels convert to FP8, FP4 or E5M6
+ * in per-token, per-block and per-channel modes).  The pages name FP4 and
+ * nothing more.  Readings taken here:
+ *  - FP4 is OCP E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; the
+ *    magnitudes of codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6 (no inf or NaN);
+ *  - the groups are the FP8 ones (1x128 per token, 128x128 per weight block),
+ *    with scale = fl32(amax / 6), 6 being the largest E2M1 magnitude;
+ *  - v = fl32(x / s) is rounded to the nearest E2M1 value, ties to the even
+ *    code, saturating at 6, keeping the sign (-0 -> 0x8);
+ *  - two codes per byte, element 2i in the low nibble and 2i+1 in the high
+ *    one (the OCP packing order), rows of K/2 bytes.
+ * ------------------------------------------------------------------------- */
+
+static double e2m1_magnitude(unsigned c) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    return mag[c & 7u];
+}
+
+/* Value of a 4-bit code. */
+double oracle_e2m1_decode(uint8_t code) { return (code & 8u) ? -e2m1_magnitude(code) : e2m1_magnitude(code); }
+
+/* Nearest E2M1 code of v (finite), ties to the even code, saturating. */
+uint8_t oracle_e2m1_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x8u : 0x0u;
+    double a = fabs((double)v);
+    if (a >= 6.0) return (uint8_t)(sign | 7u); /* saturate (far values would tie in double) */
+    unsigned best = 0;
+    for (unsigned c = 1; c < 8; c++) {
+        double dc = fabs(e2m1_magnitude(c) - a), db = fabs(e2m1_magnitude(best) - a);
+        if (dc < db || (dc == db && (c & 1u) == 0)) best = c; /* a tie goes to the even code */
+    }
+    return (uint8_t)(sign | best);
+}
+
+void oracle_e2m1_encode_array(const float *v, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e2m1_encode(v[i]);
+}
+
+static uint8_t quantize_one_fp4(float x, float s) {
+    if (s == 0.0f) return signbit(x) ? 0x8u : 0x0u; /* all-zero group */
+    float v = x / s;
+    return oracle_e2m1_encode(v);
+}
+
+/* 1x128 FP4 activations: q [M][K/2] packed, s [K/128][M]. */
+int oracle_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s) {
+    if (M < 0 || K < 0 || K % GROUP) return -1;
+    int64_t KB = K / GROUP;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            const uint16_t *g = x + m * K + kb * GROUP;
+            float amax = 0.0f;
+            for (int j = 0; j < GROUP; j++) {
+                float v = bf16_to_f32(g[j]);
+                if (!isfinite(v)) bad = 1;
+                if (fabsf(v) > amax) amax = fabsf(v);
+            }
+            float scale = amax / 6.0f;
+            s[kb * M + m] = scale;
+            for (int j = 0; j < GROUP; j += 2) {
+                uint8_t lo = quantize_one_fp4(bf16_to_f32(g[j]), scale);
+                uint8_t hi = quantize_one_fp4(bf16_to_f32(g[j + 1]), scale);
+                q[m * (K / 2) + (kb * GROUP + j) / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* 128x128 FP4 weights: q [N][K/2] packed, s [N/128][K/128]. */
+int oracle_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s) {
+    if (N < 0 || K < 0 || N % GROUP || K % GROUP) return -1;
+    int64_t NB = N / GROUP, KB = K / GROUP;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : bad)
+    for (int64_t nb = 0; nb < NB; nb++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            float amax = 0.0f;
+            for (int i = 0; i < GROUP; i++) {
+                const uint16_t *row = w + (nb * GROUP + i) * K + kb * GROUP;
+                for (int j = 0; j < GROUP; j++) {
+                    float v = bf16_to_f32(row[j]);
+                    if (!isfinite(v)) bad = 1;
+                    if (fabsf(v) > amax) amax = fabsf(v);
+                }
+            }
+            float scale = amax / 6.0f;
+            s[nb * KB + kb] = scale;
+            for (int i = 0; i < GROUP; i++) {
+                const uint16_t *row = w + (nb * GROUP + i) * K + kb * GROUP;
+                for (int j = 0; j < GROUP; j += 2) {
+                    uint8_t lo = quantize_one_fp4(bf16_to_f32(row[j]), scale);
+                    uint8_t hi = quantize_one_fp4(bf16_to_f32(row[j + 1]), scale);
+                    q[(nb * GROUP + i) * (K / 2) + (kb * GROUP + j) / 2] = (uint8_t)(lo | (hi << 4));
+                }
+            }
+        }
     }
     return bad ? -2 : 0;
 }

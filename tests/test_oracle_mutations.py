@@ -1,7 +1,7 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU; the real oracle is not
-touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe / _swiglu
+touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe / _fp4 / _swiglu
 against it until one fails.  At least one pin must fail for every planted mistake.
 """
 import os
@@ -11,6 +11,7 @@ import pytest
 import oracle
 import test_oracle_dequant as td
 import test_oracle_e4m3 as te
+import test_oracle_fp4 as tf
 import test_oracle_gemm as tg
 import test_oracle_moe as tm
 import test_oracle_swiglu as ts
@@ -49,6 +50,11 @@ MUTATIONS = {
                                   "(best < 0 || v[e] > v[best] || (v[e] == v[best] && signbit(v[best]) && !signbit(v[e])))"),
     "gather_scale_row_major": ("sa[kb * rows + r] = t >= 0", "sa[r * KB + kb] = t >= 0"),
     "gather_empty_row_copies_token_0": ("qa[r * K + k] = t >= 0 ? q[t * K + k] : 0;", "qa[r * K + k] = q[(t >= 0 ? t : 0) * K + k];"),
+    "fp4_ties_not_to_even": ("(dc == db && (c & 1u) == 0)", "(dc == db)"),
+    "fp4_divisor_4": ("float scale = amax / 6.0f;", "float scale = amax / 4.0f;"),
+    "fp4_nibbles_swapped": ("(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
+    "fp4_table_entry": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}"),
+    "fp4_no_saturation": ("    if (a >= 6.0) return (uint8_t)(sign | 7u);", ""),
     "swiglu_sigmoid_sign": ("double v = p / (1.0 + exp(-xv));", "double v = p / (1.0 + exp(xv));"),
     "swiglu_fp32_intermediate": ("double v = p / (1.0 + exp(-xv));", "double v = (double)(float)(p / (1.0 + exp(-xv)));"),
     "swiglu_tiny_gate_side_flipped": ("xv > 0 ? 1 : -1", "xv > 0 ? -1 : 1"),
@@ -85,6 +91,14 @@ def pins():
         (tm.test_gather_hand_case, {}),
         (tm.test_gather_matches_numpy_indexing, {}),
         (tm.test_gather_commutes_with_the_row_quantizer, {}),
+    ]
+    out += [
+        (tf.test_decode_table, {}),
+        (tf.test_encoder_against_exact_nearest_search, {}),
+        (tf.test_round_trip_of_every_code, {}),
+        (tf.test_hand_worked_activation_group, {}),
+        (tf.test_amax_encodes_to_six_and_negation_flips_sign_bits, {}),
+        (tf.test_error_bound_and_weight_blocks, {}),
     ]
     for case in tq.load_golden()["act_groups"]:
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
