@@ -55,12 +55,15 @@ DESCRIPTIONS = {
     "tiny": "tiny: A bf16 [128,512] with 4 outlier channels x50, W bf16 [256,512]; full path -> bf16 [128,256]",
     "dequant": "FP8 -> BF16 weight conversion with 128x128 scales: E4M3 [18432,7168] (uniform finite codes), "
                "scales [144,56] ~U(1e-4,1e-2) -> bf16 [18432,7168]",
+    "fp4": "FP4 (E2M1) quantization of the up projection's operands: A bf16 [4096,7168] ~N(0,1) with 72 outlier "
+           "channels x20 (1x128 groups), W bf16 [18432,7168] ~N(0,0.02) (128x128 blocks) -> two codes a byte",
     "dual": "forward and backward FP8 copies of the up projection's input: A bf16 [4096,7168] ~N(0,1) with 72 "
             "outlier channels x20 -> 1x128 codes [4096,7168] + codes of A^T [7168,4096] (per channel, 128 tokens)",
 }
 DEQUANT_METRIC = "FP8 -> BF16 128x128 block dequantization GB/s (% HBM peak)"
 DUAL_METRIC = "one-pass forward (1x128) + backward (1x128 of x^T) FP8 copies of a Linear input GB/s (% HBM peak)"
-BANDWIDTH_METRICS = {"dequant": DEQUANT_METRIC, "dual": DUAL_METRIC}
+FP4_METRIC = "FP4 (E2M1) 1x128 activation + 128x128 weight quantization GB/s (% HBM peak)"
+BANDWIDTH_METRICS = {"dequant": DEQUANT_METRIC, "dual": DUAL_METRIC, "fp4": FP4_METRIC}
 
 
 def log(msg):
@@ -101,6 +104,16 @@ class Workload:
         M, N, K = d["M"], d["N"], d["K"]
         self.M, self.N, self.K = M, N, K
         self.step_count = 0
+        if name == "fp4":
+            self.a, self.w = bf16(d["a"]), bf16(d["w"])
+            self.flops = 0.0
+            ab = 2 * M * K + M * K // 2 + 4 * (K // 128) * M
+            wbytes = 2 * N * K + N * K // 2 + 4 * (N // 128) * (K // 128)
+            self.bytes = ab + wbytes
+            self.kernels = [("quant_act_fp4_1x128", lambda: fq.fp8q_quant_act_fp4_1x128(self.a), {"bytes": ab}),
+                            ("quant_w_fp4_128x128", lambda: fq.fp8q_quant_w_fp4_128x128(self.w), {"bytes": wbytes})]
+            torch.cuda.synchronize()
+            return
         if name == "dual":
             self.a = bf16(d["a"])
             self.flops = 0.0
@@ -229,6 +242,20 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
     d = wk.host
     N, K = wk.N, wk.K
     lib = oracle.load()
+    if wk.name == "fp4":
+        # calibrate on 128 weight rows, then about target_s seconds' worth of weight rows and token rows
+        t0 = time.perf_counter()
+        oracle.quant_w_fp4_128x128(d["w"][:128], lib=lib)
+        oracle.quant_act_fp4_1x128(d["a"][:128], lib=lib)
+        per = time.perf_counter() - t0
+        nb = int(max(1, min(wk.M // 128, target_s / max(per, 1e-6))))
+        t1 = time.perf_counter()
+        oracle.quant_w_fp4_128x128(d["w"][:128 * nb], lib=lib)
+        oracle.quant_act_fp4_1x128(d["a"][:128 * nb], lib=lib)
+        t = time.perf_counter() - t1
+        byts = nb * 128 * (2.5 * K) * 2
+        return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+                "sample": f"{128 * nb} weight rows and {128 * nb} token rows (K={K}); {t:.1f} s"}
     if wk.name == "dual":
         # calibrate on one 128-token block, then about target_s seconds' worth of blocks
         t0 = time.perf_counter()
@@ -507,7 +534,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"dequant": "fp8_e4m3 -> bf16", "dual": "bf16 -> fp8_e4m3"}.get(args.workload, "fp8_e4m3"),
+        "dtype": {"dequant": "fp8_e4m3 -> bf16", "dual": "bf16 -> fp8_e4m3", "fp4": "bf16 -> fp4_e2m1"}.get(
+            args.workload, "fp8_e4m3"),
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,
                    "K": wk.K, "out": "bf16", "parallelism": "single GPU"},

@@ -11,6 +11,36 @@
 namespace fp8q {
 
 // ---------------------------------------------------------------------------------------------
+// FP4 (OCP E2M1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in the FP8 groupings (page "DeepSeek starts updating
+// frequently", the TileKernels quantization kernels convert to FP8, FP4 or E5M6).  The pages name FP4 only;
+// this library reads it as the same 1x128 / 128x128 groups with scale fl32(amax / 6), the nearest E2M1 value
+// (ties to the even code, saturating at 6), two codes a byte with element 2i in the low nibble.
+// ---------------------------------------------------------------------------------------------
+constexpr double kInv6 = 1.0 / 6.0;
+// fl32(amax / 6): amax has an 8-bit significand, so amax / 6 is either exact in fp32 or at least 1/6 of an
+// fp32 unit from a rounding midpoint (its bits past the 24th repeat 01 or 10), far beyond the double
+// product's error: rounding that product to fp32 gives the correctly rounded quotient.
+__device__ __forceinline__ float group_scale_fp4(float amax) { return (float)((double)amax * kInv6); }
+
+// 8 bf16 values (two packed pairs per dword, element order kept) -> 8 E2M1 codes, element 2i in the low
+// nibble.  The quotients are the exact fl32(x / s) as for FP8; v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds
+// a pair of them to the nearest E2M1 value, ties to the even code, saturating at 6, sign kept, the first in
+// the low nibble of the selected byte (checked against the oracle's E2M1 encoder on every rounding midpoint,
+// its fp32 neighbours, values past 6, subnormals, signed zeros and 10^5 random values).
+__device__ __forceinline__ uint32_t quant8_fp4(const u32x4 &v, double inv_s) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, quotient(bf16_lo(v.x), inv_s), quotient(bf16_hi(v.x), inv_s),
+                                                 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, quotient(bf16_lo(v.y), inv_s), quotient(bf16_hi(v.y), inv_s),
+                                                 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, quotient(bf16_lo(v.z), inv_s), quotient(bf16_hi(v.z), inv_s),
+                                                 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, quotient(bf16_lo(v.w), inv_s), quotient(bf16_hi(v.w), inv_s),
+                                                 1.0f, 3);
+    return r;
+}
+
+// ---------------------------------------------------------------------------------------------
 // 1x128 activations.  A 128-element group (256 bytes of bf16) is spread over the 16 lanes of a DPP row,
 // 8 elements per lane, so its max-abs is 4 row rotations.  Lane l of a wave works on K-block
 // 4 kq + l / 16 (kq = the workgroup's K-block quad) of 4 consecutive tokens, one token per load: each load
@@ -18,6 +48,7 @@ namespace fp8q {
 // 512 code bytes contiguously.  A workgroup (4 waves) covers 16 tokens x 4 K-blocks; its scales are 16
 // consecutive tokens of the K-block-major s_a layout for each of the 4 K-blocks.
 // ---------------------------------------------------------------------------------------------
+template <bool FP4>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
     const int lane = threadIdx.x & 63;
@@ -46,14 +77,18 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
         amax = absmax2(amax, v[j].z);
         amax = absmax2(amax, v[j].w);
         amax = row16_max(amax);
-        const float sc = group_scale(amax);
+        const float sc = FP4 ? group_scale_fp4(amax) : group_scale(amax);
         const double inv = scale_reciprocal(sc);
         const int64_t m = row0 + j;
         if (m < M && kb_ok) {
-            uint2 o;
-            o.x = quant4(v[j].x, v[j].y, inv);
-            o.y = quant4(v[j].z, v[j].w, inv);
-            *reinterpret_cast<uint2 *>(q + m * K + kb * 128 + i * 8) = o;
+            if constexpr (FP4) {
+                *reinterpret_cast<uint32_t *>(q + m * (K / 2) + kb * 64 + i * 4) = quant8_fp4(v[j], inv);
+            } else {
+                uint2 o;
+                o.x = quant4(v[j].x, v[j].y, inv);
+                o.y = quant4(v[j].z, v[j].w, inv);
+                *reinterpret_cast<uint2 *>(q + m * K + kb * 128 + i * 8) = o;
+            }
             if (i == 0) s[kb * M + m] = sc;
         }
     }
@@ -282,6 +317,7 @@ __global__ __launch_bounds__(256) void swiglu_bf16_kernel(const uint16_t *__rest
 // 16-byte chunk (t % 16) of block row (t / 16 + 16 i): 16 threads cover a 256-byte row, one
 // instruction covers 16 rows.  The block max is a wave reduction plus a 4-entry LDS exchange.
 // ---------------------------------------------------------------------------------------------
+template <bool FP4>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
     __shared__ float wave_amax[4];
@@ -309,16 +345,23 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
     if ((tid & 63) == 0) wave_amax[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
-    const float sc = group_scale(amax);
+    const float sc = FP4 ? group_scale_fp4(amax) : group_scale(amax);
     const double inv = scale_reciprocal(sc);
 
-    uint8_t *dst = q + (nb * 128) * K + kb * 128 + chunk * 8;
+    if constexpr (FP4) {
+        uint8_t *dst = q + (nb * 128) * (K / 2) + kb * 64 + chunk * 4;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint2 o;
-        o.x = quant4(v[i].x, v[i].y, inv);
-        o.y = quant4(v[i].z, v[i].w, inv);
-        *reinterpret_cast<uint2 *>(dst + (int64_t)(r0 + 16 * i) * K) = o;
+        for (int i = 0; i < 8; i++)
+            *reinterpret_cast<uint32_t *>(dst + (int64_t)(r0 + 16 * i) * (K / 2)) = quant8_fp4(v[i], inv);
+    } else {
+        uint8_t *dst = q + (nb * 128) * K + kb * 128 + chunk * 8;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint2 o;
+            o.x = quant4(v[i].x, v[i].y, inv);
+            o.y = quant4(v[i].z, v[i].w, inv);
+            *reinterpret_cast<uint2 *>(dst + (int64_t)(r0 + 16 * i) * K) = o;
+        }
     }
     if (tid == 0) s[nb * KB + kb] = sc;
 }
@@ -369,14 +412,29 @@ hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8
                                   hipStream_t stream) {
     const int64_t KQ = (K / 128 + 3) / 4;
     const int64_t blocks = ((M + 15) / 16) * KQ;  // 1-D grid: K-block quad fastest, 16 tokens per workgroup
-    quant_act_1x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    quant_act_1x128_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
+                                      hipStream_t stream) {
+    const int64_t KQ = (K / 128 + 3) / 4;
+    const int64_t blocks = ((M + 15) / 16) * KQ;
+    quant_act_1x128_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                   hipStream_t stream) {
     const int64_t blocks = (N / 128) * (K / 128);  // 1-D grid: K-block fastest
-    quant_w_128x128_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    quant_w_128x128_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                                      hipStream_t stream) {
+    const int64_t blocks = (N / 128) * (K / 128);
+    quant_w_128x128_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
     return hipGetLastError();
 }
 

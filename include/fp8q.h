@@ -71,6 +71,20 @@ typedef enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 } fp8q_out_dtype;
  * Requires M >= 0, K >= 0, K % 128 == 0. */
 int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* FP4 quantization in the FP8 groupings (page "DeepSeek starts updating
+ * frequently", the list of TileKernels features: the quantization kernels
+ * convert to FP8, FP4 or E5M6).  The pages name FP4 only; this library reads it
+ * as OCP E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6) with the FP8 groups and scale = fl32(amax / 6):
+ *   q = E2M1_RNE_saturating(fl32(x / s)), -0 -> code 0x8, two codes a byte,
+ *   element 2i in the low nibble and 2i+1 in the high nibble.
+ * Activations (1x128):  x bf16 [M, K] -> q [M, K/2] bytes, s fp32 [K/128][M]
+ * Weights (128x128):    w bf16 [N, K] -> q [N, K/2] bytes, s fp32 [N/128][K/128]
+ * Requires K % 128 == 0 (and N % 128 == 0 for weights), 16-byte aligned
+ * pointers. */
+int fp8q_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
+int fp8q_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
+
 /* Forward and backward FP8 copies of a Linear input in one pass (the passage
  * on caching the Linear's input in FP8 for the backward pass).  The backward
  * pass contracts the input over tokens (dW = dY^T x), so its FP8 copy needs

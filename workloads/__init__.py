@@ -160,5 +160,12 @@ def dual(M=4096, K=7168):
     return {"name": "dual", "a": a, "outlier_channels": ch, "M": M, "N": 0, "K": K}
 
 
+def fp4(M=4096, N=18432, K=7168):
+    """The up projection's activation and weight (same recipes and seed as the up workload), for FP4."""
+    d = dense_up(M, N, K)
+    d["name"] = "fp4"
+    return d
+
+
 WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant,
-             "dual": dual}
+             "dual": dual, "fp4": fp4}
