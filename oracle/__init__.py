@@ -87,6 +87,8 @@ def load(path: str | None = None):
         lib.oracle_quant_act_fp4_1x128.restype = ctypes.c_int
         lib.oracle_quant_w_fp4_128x128.argtypes = [P, I64, I64, P, P]
         lib.oracle_quant_w_fp4_128x128.restype = ctypes.c_int
+        lib.oracle_quant_w_per_channel.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_w_per_channel.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -443,4 +445,16 @@ def quant_w_fp4_128x128(w_bits, lib=None):
     q = np.empty((N, K // 2), dtype=np.uint8)
     s = np.empty((N // 128, K // 128), dtype=np.float32)
     _check(lib.oracle_quant_w_fp4_128x128(_ptr(w), N, K, _ptr(q), _ptr(s)), "quant_w_fp4_128x128")
+    return q, s
+
+
+def quant_w_per_channel(w_bits, lib=None):
+    """Per-channel FP8 weights: one scale per output channel (row of ``w [N, K]``) over all K ->
+    ``(q uint8 [N, K], s float32 [N])``."""
+    lib = lib or load()
+    w = _c(w_bits, np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty(N, dtype=np.float32)
+    _check(lib.oracle_quant_w_per_channel(_ptr(w), N, K, _ptr(q), _ptr(s)), "quant_w_per_channel")
     return q, s

@@ -49,6 +49,8 @@
  *  - FP4 (E2M1) quantization in the FP8 groupings (same page and list: the
  *    quantization kernels convert to FP8, FP4 or E5M6); readings beside the
  *    functions.
+ *  - Per-channel FP8 weights (same list: per-channel mode): one scale per
+ *    output channel over the whole row.
  *  - Fused SwiGLU + 1x128 quantization (same page and list: the quantization
  *    kernels combine SwiGLU with quantization): h = bf16(SiLU(x) * y), the
  *    exact value rounded once, then the 1x128 activation quantizer on h.
@@ -588,6 +590,31 @@ int oracle_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t 
                 }
             }
         }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-channel FP8 weights (page "DeepSeek starts updating frequently", the
+ * list of TileKernels features: per-token, per-block and per-channel modes).
+ * Reading: one scale per output channel, i.e. per row of W [N, K] over all K:
+ * s[n] = fl32(max_k |w[n,k]| / 448), q[n,k] = E4M3(fl32(w[n,k] / s[n])).
+ * ------------------------------------------------------------------------- */
+int oracle_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s) {
+    if (N < 0 || K < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        const uint16_t *row = w + n * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float v = bf16_to_f32(row[k]);
+            if (!isfinite(v)) bad = 1;
+            if (fabsf(v) > amax) amax = fabsf(v);
+        }
+        float scale = amax / 448.0f;
+        s[n] = scale;
+        for (int64_t k = 0; k < K; k++) q[n * K + k] = quantize_one(bf16_to_f32(row[k]), scale);
     }
     return bad ? -2 : 0;
 }

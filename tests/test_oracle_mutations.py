@@ -14,6 +14,7 @@ import test_oracle_e4m3 as te
 import test_oracle_fp4 as tf
 import test_oracle_gemm as tg
 import test_oracle_moe as tm
+import test_oracle_per_channel as tp
 import test_oracle_swiglu as ts
 import test_oracle_quant as tq
 
@@ -55,6 +56,10 @@ MUTATIONS = {
     "fp4_nibbles_swapped": ("(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
     "fp4_table_entry": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}"),
     "fp4_no_saturation": ("    if (a >= 6.0) return (uint8_t)(sign | 7u);", ""),
+    "per_channel_amax_first_group": ("        for (int64_t k = 0; k < K; k++) {\n            float v = bf16_to_f32(row[k]);\n            if (!isfinite(v)) bad = 1;\n            if (fabsf(v) > amax) amax = fabsf(v);",
+                                     "        for (int64_t k = 0; k < K && k < 128; k++) {\n            float v = bf16_to_f32(row[k]);\n            if (!isfinite(v)) bad = 1;\n            if (fabsf(v) > amax) amax = fabsf(v);"),
+    "per_channel_signed_amax": ("            if (fabsf(v) > amax) amax = fabsf(v);\n        }\n        float scale = amax / 448.0f;\n        s[n] = scale;",
+                                "            if (v > amax) amax = v;\n        }\n        float scale = amax / 448.0f;\n        s[n] = scale;"),
     "swiglu_sigmoid_sign": ("double v = p / (1.0 + exp(-xv));", "double v = p / (1.0 + exp(xv));"),
     "swiglu_fp32_intermediate": ("double v = p / (1.0 + exp(-xv));", "double v = (double)(float)(p / (1.0 + exp(-xv)));"),
     "swiglu_tiny_gate_side_flipped": ("xv > 0 ? 1 : -1", "xv > 0 ? -1 : 1"),
@@ -99,6 +104,9 @@ def pins():
         (tf.test_hand_worked_activation_group, {}),
         (tf.test_amax_encodes_to_six_and_negation_flips_sign_bits, {}),
         (tf.test_error_bound_and_weight_blocks, {}),
+        (tp.test_hand_worked_row, {}),
+        (tp.test_matches_rowwise_numpy, {}),
+        (tp.test_equals_one_group_per_row_when_k_is_128, {}),
     ]
     for case in tq.load_golden()["act_groups"]:
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
