@@ -7,6 +7,7 @@ this package is its Python binding.  Entry points (same names as the C functions
   fp8q_quant_act_dual(x)                       bf16 [M, K] -> the 1x128 copies of x and of x^T (backward)
   fp8q_quant_act_fp4_1x128(x), fp8q_quant_w_fp4_128x128(w)   FP4 (E2M1) in the same groups, two codes a byte
   fp8q_quant_w_128x128(w)                      bf16 [N, K] -> (E4M3 [N, K], fp32 scales [N/128, K/128])
+  fp8q_quant_w_per_channel(w)                  bf16 [N, K] -> (E4M3 [N, K], one fp32 scale per output channel [N])
   fp8q_swiglu_quant_act_1x128(x, y)            bf16 gate, up [M, K] -> 1x128 quantization of bf16(SiLU(x) * y)
   fp8q_swiglu_bf16(x, y)                       the bf16 intermediate SiLU(x) * y alone
   fp8q_gemm_blockscaled(qa, sa, qw, sw)        -> C = A W^T, bf16 or fp32 [M, N]
@@ -30,6 +31,7 @@ from ._binding import (  # noqa: F401
     fp8q_quant_act_fp4_1x128,
     fp8q_quant_w_128x128,
     fp8q_quant_w_fp4_128x128,
+    fp8q_quant_w_per_channel,
     fp8q_swiglu_bf16,
     fp8q_swiglu_quant_act_1x128,
     load_library,

@@ -40,6 +40,7 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_quant_act_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         lib.fp8q_quant_act_fp4_1x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_quant_w_fp4_128x128.argtypes = [P, I64, I64, P, P, P]
+        lib.fp8q_quant_w_per_channel.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
@@ -47,7 +48,7 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
                   lib.fp8q_swiglu_bf16, lib.fp8q_quant_act_dual, lib.fp8q_quant_act_fp4_1x128,
-                  lib.fp8q_quant_w_fp4_128x128,
+                  lib.fp8q_quant_w_fp4_128x128, lib.fp8q_quant_w_per_channel,
                   lib.fp8q_gemm_blockscaled,
                   lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
                   lib.fp8q_moe_gather_fp8):
@@ -153,6 +154,25 @@ def fp8q_quant_w_fp4_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: 
         raise ValueError("output tensors have the wrong size")
     _check(load_library().fp8q_quant_w_fp4_128x128(_ptr(w), N, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
            "fp8q_quant_w_fp4_128x128")
+    return q, s
+
+
+def fp8q_quant_w_per_channel(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                             stream=None):
+    """Per-channel FP8 weight quantization, one scale per output channel.  ``w`` bf16 [N, K] (K a multiple of
+    8) -> ``(q uint8 [N, K], s float32 [N])``."""
+    _need(w, "w", _BF16, 2)
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _need(q, "q", (torch.uint8,))
+    _need(s, "s", (torch.float32,))
+    if q.numel() != N * K or s.numel() != N:
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_quant_w_per_channel(_ptr(w), N, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
+           "fp8q_quant_w_per_channel")
     return q, s
 
 

@@ -108,6 +108,17 @@ int fp8q_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q
     return finish(fp8q::launch_quant_w_fp4_128x128(w, N, K, q, s, static_cast<hipStream_t>(stream)));
 }
 
+int fp8q_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream) {
+    if (N < 0 || K < 0 || K % 8) return FP8Q_ERR_SHAPE;
+    if (N == 0) return FP8Q_OK;
+    if (!s || (K > 0 && (!w || !q))) return FP8Q_ERR_NULL;  // K == 0: only the (zero) scales are written
+    if (!aligned4(s) || (K > 0 && (!aligned16(w) || !aligned16(q)))) return FP8Q_ERR_ALIGN;
+    if ((N + 3) / 4 > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_quant_w_per_channel(w, N, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
 int fp8q_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt, float *st,
                         void *stream) {
     if (M < 0 || K < 0 || M % 128 || K % 128) return FP8Q_ERR_SHAPE;

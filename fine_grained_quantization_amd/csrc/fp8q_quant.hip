@@ -366,6 +366,61 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
     if (tid == 0) s[nb * KB + kb] = sc;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Per-channel FP8 weights (page "DeepSeek starts updating frequently", the TileKernels quantization modes:
+// per token, per block, per channel).  Read as one scale per output channel: row n of W [N, K] over all of
+// K, s[n] = fl32(amax_n / 448), the codes as in the grouped modes.  One wave per row (4 rows a workgroup),
+// so the row's max-abs is a wave reduction with no LDS or barrier.  Lane l holds the row's 16-byte chunks
+// l, l + 64, ...: the first kRowChunks of them stay in registers between the max and the encode (rows up
+// to 64 * kRowChunks * 8 = 8192 elements are read once); chunks past them are read again for the encode
+// (from L2: the row was just read).  Each load and store instruction of a wave is contiguous.
+// ---------------------------------------------------------------------------------------------
+constexpr int kRowChunks = 16;
+
+__global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t *__restrict__ w, int64_t N,
+                                                                  int64_t K, uint8_t *__restrict__ q,
+                                                                  float *__restrict__ s) {
+    const int lane = threadIdx.x & 63;
+    const int64_t n = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (n >= N) return;  // whole waves leave
+    const int64_t chunks = K >> 3;
+    const uint16_t *row = w + n * K;
+    uint8_t *dst = q + n * K;
+
+    u32x4 v[kRowChunks];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; j++) {
+        const int64_t c = lane + 64 * j;
+        v[j] = c < chunks ? load_stream16(row + c * 8) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kRowChunks; j++) {
+        amax = absmax2(amax, v[j].x);
+        amax = absmax2(amax, v[j].y);
+        amax = absmax2(amax, v[j].z);
+        amax = absmax2(amax, v[j].w);
+    }
+    for (int64_t c = lane + 64 * kRowChunks; c < chunks; c += 64) {
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(row + c * 8);
+        amax = absmax2(absmax2(absmax2(absmax2(amax, t.x), t.y), t.z), t.w);
+    }
+    amax = wave_max(amax);
+    const float sc = group_scale(amax);
+    const double inv = scale_reciprocal(sc);
+#pragma unroll
+    for (int j = 0; j < kRowChunks; j++) {
+        const int64_t c = lane + 64 * j;
+        if (c < chunks)
+            *reinterpret_cast<uint2 *>(dst + c * 8) = (uint2){quant4(v[j].x, v[j].y, inv), quant4(v[j].z, v[j].w, inv)};
+    }
+    for (int64_t c = lane + 64 * kRowChunks; c < chunks; c += 64) {
+        const u32x4 t = load_stream16(row + c * 8);
+        *reinterpret_cast<uint2 *>(dst + c * 8) = (uint2){quant4(t.x, t.y, inv), quant4(t.z, t.w, inv)};
+    }
+    if (lane == 0) s[n] = sc;
+}
+
 // FP8 -> BF16 weight conversion with 128x128 block scales (page "deepseek-ai/DeepSeek-V3", "How to Run
 // Locally": the published weights are FP8 and a script converts them to BF16).  Reading of the arithmetic:
 // every code times its block's scale in fp32, rounded to bf16 to nearest even, w = bf16(fl32(dec(q) * s)).
@@ -435,6 +490,13 @@ hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, u
                                       hipStream_t stream) {
     const int64_t blocks = (N / 128) * (K / 128);
     quant_w_128x128_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
+                                      hipStream_t stream) {
+    const int64_t blocks = (N + 3) / 4;  // one wave per row
+    quant_w_per_channel_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(w, N, K, q, s);
     return hipGetLastError();
 }
 

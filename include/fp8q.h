@@ -85,6 +85,18 @@ int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, fl
 int fp8q_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
 int fp8q_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* Per-channel FP8 weight quantization (page "DeepSeek starts updating
+ * frequently", the list of TileKernels features: per-token, per-block and
+ * per-channel modes).  This library reads the per-channel mode as one scale
+ * per output channel, i.e. per row of W over the whole of K:
+ *   w  : bf16 [N, K]            (input)
+ *   q  : E4M3 [N, K]            (output)
+ *   s  : fp32 [N]               (output; s[n] = fl32(max_k |w[n,k]| / 448))
+ * q[n,k] = E4M3_RNE_saturating(fl32(w[n,k] / s[n])), or a signed zero when
+ * s[n] == 0.  Requires N >= 0, K >= 0, K % 8 == 0, 16-byte aligned w and q,
+ * 4-byte aligned s; with K == 0, w and q may be null and s is set to 0. */
+int fp8q_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
+
 /* Forward and backward FP8 copies of a Linear input in one pass (the passage
  * on caching the Linear's input in FP8 for the backward pass).  The backward
  * pass contracts the input over tokens (dW = dY^T x), so its FP8 copy needs

@@ -167,5 +167,11 @@ def fp4(M=4096, N=18432, K=7168):
     return d
 
 
+def per_channel(N=18432, K=7168):
+    """The up projection's weight (same recipe and seed as the up workload), for per-channel FP8."""
+    w = normal_bf16(SEEDS["up"], T_W, (N, K), 0.02)
+    return {"name": "per_channel", "w": w, "M": 0, "N": N, "K": K}
+
+
 WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant,
-             "dual": dual, "fp4": fp4}
+             "dual": dual, "fp4": fp4, "per_channel": per_channel}
