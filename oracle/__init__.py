@@ -89,6 +89,12 @@ def load(path: str | None = None):
         lib.oracle_quant_w_fp4_128x128.restype = ctypes.c_int
         lib.oracle_quant_w_per_channel.argtypes = [P, I64, I64, P, P]
         lib.oracle_quant_w_per_channel.restype = ctypes.c_int
+        lib.oracle_e5m6_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_e5m6_decode.restype = ctypes.c_double
+        lib.oracle_e5m6_encode_array.argtypes = [P, I64, P]
+        lib.oracle_e5m6_encode_array.restype = None
+        lib.oracle_quant_act_e5m6_1x128.argtypes = [P, I64, I64, P, P]
+        lib.oracle_quant_act_e5m6_1x128.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -457,4 +463,40 @@ def quant_w_per_channel(w_bits, lib=None):
     q = np.empty((N, K), dtype=np.uint8)
     s = np.empty(N, dtype=np.float32)
     _check(lib.oracle_quant_w_per_channel(_ptr(w), N, K, _ptr(q), _ptr(s)), "quant_w_per_channel")
+    return q, s
+
+
+def e5m6_decode(codes, lib=None) -> np.ndarray:
+    """Values of 12-bit E5M6 codes (sign bit 11, exponent bits 10..6 with bias 15, mantissa bits 5..0)."""
+    lib = lib or load()
+    c = np.asarray(codes, np.uint16)
+    return np.array([lib.oracle_e5m6_decode(int(v)) for v in c.reshape(-1)]).reshape(c.shape)
+
+
+def e5m6_encode(values, lib=None) -> np.ndarray:
+    """Nearest E5M6 codes (ties to the even code, saturating at +-65024) of float32 values."""
+    lib = lib or load()
+    v = _c(values, np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.oracle_e5m6_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e5m6_unpack(q) -> np.ndarray:
+    """12-bit codes [M, K] from packed rows [M, 3K/2] (little-endian bit stream, element j at bits 12j..)."""
+    b = np.asarray(q, np.uint16).reshape(q.shape[0], -1, 3)
+    c0 = b[..., 0] | ((b[..., 1] & 0xF) << 8)
+    c1 = (b[..., 1] >> 4) | (b[..., 2] << 4)
+    return np.stack([c0, c1], axis=-1).reshape(q.shape[0], -1).astype(np.uint16)
+
+
+def quant_act_e5m6_1x128(x_bits, lib=None):
+    """1x128 E5M6 activation quantization: ``x [M, K]`` bf16 -> ``(q uint8 [M, 3K/2], s float32 [K/128, M])``,
+    scale = fl32(amax / 65024), two 12-bit codes per 3 bytes."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K // 2 * 3), dtype=np.uint8)
+    s = np.empty((K // 128, M), dtype=np.float32)
+    _check(lib.oracle_quant_act_e5m6_1x128(_ptr(x), M, K, _ptr(q), _ptr(s)), "quant_act_e5m6_1x128")
     return q, s

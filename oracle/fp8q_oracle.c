@@ -51,6 +51,9 @@
  *    functions.
  *  - Per-channel FP8 weights (same list: per-channel mode): one scale per
  *    output channel over the whole row.
+ *  - E5M6 activations (page "The Definitive Information To Deepseek", the
+ *    customized E5M6 format for certain activations; the same TileKernels
+ *    list): readings beside the functions.
  *  - Fused SwiGLU + 1x128 quantization (same page and list: the quantization
  *    kernels combine SwiGLU with quantization): h = bf16(SiLU(x) * y), the
  *    exact value rounded once, then the 1x128 activation quantizer on h.
@@ -615,6 +618,95 @@ int oracle_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t 
         float scale = amax / 448.0f;
         s[n] = scale;
         for (int64_t k = 0; k < K; k++) q[n * K + k] = quantize_one(bf16_to_f32(row[k]), scale);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * E5M6 activations (page "The Definitive Information To Deepseek", the passage
+ * naming a customized E5M6 format for certain activations; page "DeepSeek
+ * starts updating frequently", the TileKernels quantization converts to FP8,
+ * FP4 or E5M6).  The pages give the name only.  Readings taken here:
+ *  - E5M6 is the ExMy layout its name spells: sign, 5 exponent bits with the
+ *    IEEE bias 15, 6 mantissa bits, subnormals m * 2^-20 at exponent 0, and
+ *    exponent 31 reserved (inf/NaN) as in the IEEE formats with 5 exponent
+ *    bits, so the largest finite magnitude is (2 - 2^-6) * 2^15 = 65024;
+ *  - it is used in the activation grouping, 1x128 per token, with
+ *    scale = fl32(amax / 65024), v = fl32(x / s) rounded to the nearest E5M6
+ *    value, ties to the even code, saturating at 65024, sign kept (-0 -> 0x800);
+ *  - the 12-bit codes form a little-endian bit stream, element j at bits
+ *    12j..12j+11: a pair (c0, c1) fills 3 bytes c0[7:0], c0[11:8] | c1[3:0] << 4,
+ *    c1[11:4]; rows of 3K/2 bytes.
+ * ------------------------------------------------------------------------- */
+
+#define E5M6_MAX_CODE 0x7BFu /* exponent 30, mantissa 63 */
+
+/* Magnitude of the low 11 bits of a code (finite codes only). */
+static double e5m6_magnitude(unsigned c) {
+    unsigned e = (c >> 6) & 31u, m = c & 63u;
+    if (e == 0) return ldexp((double)m, -20);
+    return ldexp(64.0 + (double)m, (int)e - 15 - 6);
+}
+
+double oracle_e5m6_decode(uint16_t code) {
+    unsigned e = (code >> 6) & 31u;
+    double mag;
+    if (e == 31) mag = (code & 63u) ? NAN : INFINITY;
+    else mag = e5m6_magnitude(code);
+    return (code & 0x800u) ? -mag : mag;
+}
+
+/* Nearest E5M6 code of v (finite), ties to the even code, saturating. */
+uint16_t oracle_e5m6_encode(float v) {
+    uint16_t sign = signbit(v) ? 0x800u : 0x0u;
+    double a = fabs((double)v);
+    if (a >= e5m6_magnitude(E5M6_MAX_CODE)) return (uint16_t)(sign | E5M6_MAX_CODE);
+    /* largest code lo with magnitude <= a (magnitudes increase with the code) */
+    unsigned lo = 0, hi = E5M6_MAX_CODE;
+    while (lo < hi) {
+        unsigned mid = (lo + hi + 1) / 2;
+        if (e5m6_magnitude(mid) <= a) lo = mid;
+        else hi = mid - 1;
+    }
+    unsigned up = lo + 1;
+    double dl = a - e5m6_magnitude(lo), du = e5m6_magnitude(up) - a;
+    unsigned c = (du < dl || (du == dl && (up & 1u) == 0)) ? up : lo;
+    return (uint16_t)(sign | c);
+}
+
+void oracle_e5m6_encode_array(const float *v, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e5m6_encode(v[i]);
+}
+
+/* 1x128 E5M6 activations: q [M][3K/2] bytes, s [K/128][M]. */
+int oracle_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s) {
+    if (M < 0 || K < 0 || K % GROUP) return -1;
+    int64_t KB = K / GROUP, row_bytes = K / 2 * 3;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t kb = 0; kb < KB; kb++) {
+            const uint16_t *g = x + m * K + kb * GROUP;
+            float amax = 0.0f;
+            for (int j = 0; j < GROUP; j++) {
+                float v = bf16_to_f32(g[j]);
+                if (!isfinite(v)) bad = 1;
+                if (fabsf(v) > amax) amax = fabsf(v);
+            }
+            float scale = amax / 65024.0f;
+            s[kb * M + m] = scale;
+            uint8_t *out = q + m * row_bytes + kb * (GROUP / 2 * 3);
+            for (int j = 0; j < GROUP; j += 2) {
+                uint16_t c[2];
+                for (int t = 0; t < 2; t++) {
+                    float xv = bf16_to_f32(g[j + t]);
+                    c[t] = scale == 0.0f ? (uint16_t)(signbit(xv) ? 0x800u : 0u) : oracle_e5m6_encode(xv / scale);
+                }
+                out[j / 2 * 3 + 0] = (uint8_t)(c[0] & 0xFFu);
+                out[j / 2 * 3 + 1] = (uint8_t)((c[0] >> 8) | ((c[1] & 0xFu) << 4));
+                out[j / 2 * 3 + 2] = (uint8_t)(c[1] >> 4);
+            }
+        }
     }
     return bad ? -2 : 0;
 }

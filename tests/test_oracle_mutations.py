@@ -1,7 +1,8 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU; the real oracle is not
-touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe / _fp4 / _swiglu
+touched), compiles it, and runs the pins from test_oracle_e4m3 / _quant / _gemm / _dequant / _moe / _fp4 /
+_per_channel / _e5m6 / _swiglu
 against it until one fails.  At least one pin must fail for every planted mistake.
 """
 import os
@@ -11,6 +12,7 @@ import pytest
 import oracle
 import test_oracle_dequant as td
 import test_oracle_e4m3 as te
+import test_oracle_e5m6 as t56
 import test_oracle_fp4 as tf
 import test_oracle_gemm as tg
 import test_oracle_moe as tm
@@ -60,6 +62,12 @@ MUTATIONS = {
                                      "        for (int64_t k = 0; k < K && k < 128; k++) {\n            float v = bf16_to_f32(row[k]);\n            if (!isfinite(v)) bad = 1;\n            if (fabsf(v) > amax) amax = fabsf(v);"),
     "per_channel_signed_amax": ("            if (fabsf(v) > amax) amax = fabsf(v);\n        }\n        float scale = amax / 448.0f;\n        s[n] = scale;",
                                 "            if (v > amax) amax = v;\n        }\n        float scale = amax / 448.0f;\n        s[n] = scale;"),
+    "e5m6_bias_14": ("return ldexp(64.0 + (double)m, (int)e - 15 - 6);", "return ldexp(64.0 + (double)m, (int)e - 14 - 6);"),
+    "e5m6_no_subnormals": ("if (e == 0) return ldexp((double)m, -20);", "if (0) return ldexp((double)m, -20);"),
+    "e5m6_ties_away": ("(du == dl && (up & 1u) == 0)", "(du == dl)"),
+    "e5m6_divisor_fp16_max": ("float scale = amax / 65024.0f;", "float scale = amax / 65504.0f;"),
+    "e5m6_pair_order_swapped": ("out[j / 2 * 3 + 1] = (uint8_t)((c[0] >> 8) | ((c[1] & 0xFu) << 4));",
+                                "out[j / 2 * 3 + 1] = (uint8_t)((c[1] >> 8) | ((c[0] & 0xFu) << 4));"),
     "swiglu_sigmoid_sign": ("double v = p / (1.0 + exp(-xv));", "double v = p / (1.0 + exp(xv));"),
     "swiglu_fp32_intermediate": ("double v = p / (1.0 + exp(-xv));", "double v = (double)(float)(p / (1.0 + exp(-xv)));"),
     "swiglu_tiny_gate_side_flipped": ("xv > 0 ? 1 : -1", "xv > 0 ? -1 : 1"),
@@ -107,6 +115,12 @@ def pins():
         (tp.test_hand_worked_row, {}),
         (tp.test_matches_rowwise_numpy, {}),
         (tp.test_equals_one_group_per_row_when_k_is_128, {}),
+        (t56.test_decode_equals_half_precision_with_four_zero_bits, {}),
+        (t56.test_hand_worked_group_and_byte_layout, {}),
+        (t56.test_encoder_on_every_half_precision_value, {}),
+        (t56.test_encoder_against_exact_search_on_midpoints, {}),
+        (t56.test_amax_encodes_to_the_largest_code_and_negation_flips_sign_bits, {}),
+        (t56.test_error_bound_and_scales, {}),
     ]
     for case in tq.load_golden()["act_groups"]:
         out.append((tq.test_hand_worked_activation_groups, {"case": case}))
