@@ -57,6 +57,8 @@ DESCRIPTIONS = {
                "scales [144,56] ~U(1e-4,1e-2) -> bf16 [18432,7168]",
     "fp4": "FP4 (E2M1) quantization of the up projection's operands: A bf16 [4096,7168] ~N(0,1) with 72 outlier "
            "channels x20 (1x128 groups), W bf16 [18432,7168] ~N(0,0.02) (128x128 blocks) -> two codes a byte",
+    "e5m6": "E5M6 1x128 quantization of the up projection's input: A bf16 [4096,7168] ~N(0,1) with 72 outlier "
+            "channels x20 -> 12-bit codes, two per 3 bytes, + 1x128 fp32 scales",
     "per_channel": "per-channel FP8 quantization of the up projection's weight: W bf16 [18432,7168] ~N(0,0.02) "
                    "-> E4M3 [18432,7168] + one fp32 scale per output channel",
     "dual": "forward and backward FP8 copies of the up projection's input: A bf16 [4096,7168] ~N(0,1) with 72 "
@@ -66,8 +68,9 @@ DEQUANT_METRIC = "FP8 -> BF16 128x128 block dequantization GB/s (% HBM peak)"
 DUAL_METRIC = "one-pass forward (1x128) + backward (1x128 of x^T) FP8 copies of a Linear input GB/s (% HBM peak)"
 FP4_METRIC = "FP4 (E2M1) 1x128 activation + 128x128 weight quantization GB/s (% HBM peak)"
 PER_CHANNEL_METRIC = "per-channel FP8 weight quantization GB/s (% HBM peak)"
+E5M6_METRIC = "E5M6 1x128 activation quantization GB/s (% HBM peak)"
 BANDWIDTH_METRICS = {"dequant": DEQUANT_METRIC, "dual": DUAL_METRIC, "fp4": FP4_METRIC,
-                     "per_channel": PER_CHANNEL_METRIC}
+                     "per_channel": PER_CHANNEL_METRIC, "e5m6": E5M6_METRIC}
 
 
 def log(msg):
@@ -116,6 +119,14 @@ class Workload:
             self.bytes = ab + wbytes
             self.kernels = [("quant_act_fp4_1x128", lambda: fq.fp8q_quant_act_fp4_1x128(self.a), {"bytes": ab}),
                             ("quant_w_fp4_128x128", lambda: fq.fp8q_quant_w_fp4_128x128(self.w), {"bytes": wbytes})]
+            torch.cuda.synchronize()
+            return
+        if name == "e5m6":
+            self.a = bf16(d["a"])
+            self.flops = 0.0
+            self.bytes = 2 * M * K + M * K // 2 * 3 + 4 * (K // 128) * M
+            self.kernels = [("quant_act_e5m6_1x128", lambda: fq.fp8q_quant_act_e5m6_1x128(self.a),
+                             {"bytes": self.bytes})]
             torch.cuda.synchronize()
             return
         if name == "per_channel":
@@ -268,6 +279,18 @@ def cpu_baseline(wk: Workload, target_s: float = 12.0):
         byts = nb * 128 * (2.5 * K) * 2
         return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
                 "sample": f"{128 * nb} weight rows and {128 * nb} token rows (K={K}); {t:.1f} s"}
+    if wk.name == "e5m6":
+        # calibrate on 128 token rows, then about target_s seconds' worth of rows
+        t0 = time.perf_counter()
+        oracle.quant_act_e5m6_1x128(d["a"][:128], lib=lib)
+        per = time.perf_counter() - t0
+        nb = int(max(1, min(wk.M // 128, target_s / max(per, 1e-6))))
+        t1 = time.perf_counter()
+        oracle.quant_act_e5m6_1x128(d["a"][:128 * nb], lib=lib)
+        t = time.perf_counter() - t1
+        byts = wk.bytes * nb * 128 / wk.M
+        return {"value": byts / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+                "sample": f"{128 * nb} of the {wk.M} token rows (K={K}); {t:.1f} s"}
     if wk.name == "per_channel":
         # calibrate on 128 weight rows, then about target_s seconds' worth of rows
         t0 = time.perf_counter()
@@ -410,7 +433,9 @@ GEMM_SOURCES = ("fine_grained_quantization_amd/csrc/fp8q_gemm.hip", "fine_graine
 QUANT_SOURCES = ("fine_grained_quantization_amd/csrc/fp8q_quant.hip", "fine_grained_quantization_amd/csrc/fp8q_device.h")
 # The sources each reported kernel is built from (its recorded traffic is stale once they change).
 KERNEL_SOURCES = {"gemm_blockscaled": GEMM_SOURCES, "grouped_gemm_blockscaled": GEMM_SOURCES,
-                  "dequant_w_128x128": QUANT_SOURCES}
+                  "dequant_w_128x128": QUANT_SOURCES, "quant_act_dual": QUANT_SOURCES,
+                  "quant_w_fp4_128x128": QUANT_SOURCES, "quant_w_per_channel": QUANT_SOURCES,
+                  "quant_act_e5m6_1x128": QUANT_SOURCES}
 
 
 def sources_sha256(paths=GEMM_SOURCES):
@@ -559,7 +584,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"dequant": "fp8_e4m3 -> bf16", "dual": "bf16 -> fp8_e4m3", "fp4": "bf16 -> fp4_e2m1",
-                  "per_channel": "bf16 -> fp8_e4m3"}.get(
+                  "per_channel": "bf16 -> fp8_e4m3", "e5m6": "bf16 -> e5m6"}.get(
             args.workload, "fp8_e4m3"),
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,

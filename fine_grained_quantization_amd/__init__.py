@@ -6,6 +6,7 @@ this package is its Python binding.  Entry points (same names as the C functions
   fp8q_quant_act_1x128(x)                      bf16 [M, K] -> (E4M3 [M, K], fp32 scales [K/128, M])
   fp8q_quant_act_dual(x)                       bf16 [M, K] -> the 1x128 copies of x and of x^T (backward)
   fp8q_quant_act_fp4_1x128(x), fp8q_quant_w_fp4_128x128(w)   FP4 (E2M1) in the same groups, two codes a byte
+  fp8q_quant_act_e5m6_1x128(x)                 bf16 [M, K] -> 12-bit E5M6 codes, two per 3 bytes, 1x128 scales
   fp8q_quant_w_128x128(w)                      bf16 [N, K] -> (E4M3 [N, K], fp32 scales [N/128, K/128])
   fp8q_quant_w_per_channel(w)                  bf16 [N, K] -> (E4M3 [N, K], one fp32 scale per output channel [N])
   fp8q_swiglu_quant_act_1x128(x, y)            bf16 gate, up [M, K] -> 1x128 quantization of bf16(SiLU(x) * y)
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     fp8q_moe_route_topk,
     fp8q_quant_act_1x128,
     fp8q_quant_act_dual,
+    fp8q_quant_act_e5m6_1x128,
     fp8q_quant_act_fp4_1x128,
     fp8q_quant_w_128x128,
     fp8q_quant_w_fp4_128x128,

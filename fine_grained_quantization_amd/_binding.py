@@ -41,6 +41,7 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_quant_act_fp4_1x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_quant_w_fp4_128x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_quant_w_per_channel.argtypes = [P, I64, I64, P, P, P]
+        lib.fp8q_quant_act_e5m6_1x128.argtypes = [P, I64, I64, P, P, P]
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
@@ -48,7 +49,7 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
                   lib.fp8q_swiglu_bf16, lib.fp8q_quant_act_dual, lib.fp8q_quant_act_fp4_1x128,
-                  lib.fp8q_quant_w_fp4_128x128, lib.fp8q_quant_w_per_channel,
+                  lib.fp8q_quant_w_fp4_128x128, lib.fp8q_quant_w_per_channel, lib.fp8q_quant_act_e5m6_1x128,
                   lib.fp8q_gemm_blockscaled,
                   lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
                   lib.fp8q_moe_gather_fp8):
@@ -154,6 +155,25 @@ def fp8q_quant_w_fp4_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: 
         raise ValueError("output tensors have the wrong size")
     _check(load_library().fp8q_quant_w_fp4_128x128(_ptr(w), N, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
            "fp8q_quant_w_fp4_128x128")
+    return q, s
+
+
+def fp8q_quant_act_e5m6_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                              stream=None):
+    """1x128 E5M6 activation quantization.  ``x`` bf16 [M, K] -> ``(q uint8 [M, 3K/2], s float32 [K/128, M])``,
+    two 12-bit codes per 3 bytes (element j at bits 12j of its row)."""
+    _need(x, "x", _BF16, 2)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K // 2 * 3), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _need(q, "q", (torch.uint8,))
+    _need(s, "s", (torch.float32,))
+    if q.numel() != M * (K // 2 * 3) or s.numel() != M * (K // 128):
+        raise ValueError("output tensors have the wrong size")
+    _check(load_library().fp8q_quant_act_e5m6_1x128(_ptr(x), M, K, _ptr(q), _ptr(s), _stream_ptr(stream)),
+           "fp8q_quant_act_e5m6_1x128")
     return q, s
 
 

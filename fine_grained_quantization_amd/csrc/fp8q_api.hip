@@ -108,6 +108,17 @@ int fp8q_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q
     return finish(fp8q::launch_quant_w_fp4_128x128(w, N, K, q, s, static_cast<hipStream_t>(stream)));
 }
 
+int fp8q_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream) {
+    if (M < 0 || K < 0 || K % 128) return FP8Q_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return FP8Q_ERR_ALIGN;
+    if (((M + 15) / 16) * ((K / 128 + 3) / 4) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_quant_act_e5m6_1x128(x, M, K, q, s, static_cast<hipStream_t>(stream)));
+}
+
 int fp8q_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream) {
     if (N < 0 || K < 0 || K % 8) return FP8Q_ERR_SHAPE;
     if (N == 0) return FP8Q_OK;

@@ -19,6 +19,8 @@ hipError_t launch_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, u
                                       hipStream_t stream);
 hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                       hipStream_t stream);
+hipError_t launch_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
+                                       hipStream_t stream);
 hipError_t launch_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                       hipStream_t stream);
 hipError_t launch_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t K, uint16_t *w,

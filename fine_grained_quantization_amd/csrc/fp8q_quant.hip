@@ -41,6 +41,43 @@ __device__ __forceinline__ uint32_t quant8_fp4(const u32x4 &v, double inv_s) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// E5M6 (sign, 5 exponent bits with bias 15, 6 mantissa bits, subnormals m * 2^-20, exponent 31 reserved:
+// largest finite 65024) in the 1x128 activation groups (page "The Definitive Information To Deepseek", the
+// customized E5M6 format for certain activations; the TileKernels list on "DeepSeek starts updating
+// frequently").  The pages give the name only; this library reads it as that layout with scale
+// fl32(amax / 65024), nearest even, saturating, and the 12-bit codes as a little-endian bit stream.
+// ---------------------------------------------------------------------------------------------
+constexpr double kInv65024 = 1.0 / 65024.0;
+// fl32(amax / 65024) = fl32(amax * RN64(1/65024)): 65024 = 127 * 2^9 and amax has an 8-bit significand, so
+// the quotient is exact in fp32 (amax a multiple of 127) or its bits past the 24th repeat with period 7, at
+// least 2^-8 of an fp32 unit from any midpoint, far beyond the double product's error.
+__device__ __forceinline__ float group_scale_e5m6(float amax) { return (float)((double)amax * kInv65024); }
+
+// E5M6 code of an fp32 value v with |v| <= 65024 (1 + 2^-23): normal results round the fp32 pattern to 6
+// mantissa bits (nearest even, a carry runs into the exponent) and rebias 127 -> 15; below 2^-14 the code
+// is the subnormal count v * 2^20 (exact) rounded to nearest even.  Checked on the CPU against the oracle's
+// encoder on every 7th fp32 pattern up to 65024 (1 + 2^-23), both signs, and every midpoint.
+__device__ __forceinline__ uint32_t e5m6_code(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t normal = min(((a + 0xFFFFu + ((a >> 17) & 1u)) >> 17) - (112u << 6), 0x7BFu);
+    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1p20f);
+    return ((b >> 20) & 0x800u) | (a >= 0x38800000u ? normal : sub);
+}
+
+// 8 bf16 values (two packed pairs per dword) -> 8 codes of 12 bits, element j at bits 12j of 96.
+__device__ __forceinline__ uint3 quant8_e5m6(const u32x4 &v, double inv_s) {
+    const uint32_t c0 = e5m6_code(quotient(bf16_lo(v.x), inv_s)), c1 = e5m6_code(quotient(bf16_hi(v.x), inv_s));
+    const uint32_t c2 = e5m6_code(quotient(bf16_lo(v.y), inv_s)), c3 = e5m6_code(quotient(bf16_hi(v.y), inv_s));
+    const uint32_t c4 = e5m6_code(quotient(bf16_lo(v.z), inv_s)), c5 = e5m6_code(quotient(bf16_hi(v.z), inv_s));
+    const uint32_t c6 = e5m6_code(quotient(bf16_lo(v.w), inv_s)), c7 = e5m6_code(quotient(bf16_hi(v.w), inv_s));
+    return (uint3){c0 | (c1 << 12) | (c2 << 24), (c2 >> 8) | (c3 << 4) | (c4 << 16) | (c5 << 28),
+                   (c5 >> 4) | (c6 << 8) | (c7 << 20)};
+}
+
+enum : int { kFmtFp8 = 0, kFmtFp4 = 1, kFmtE5M6 = 2 };
+
+// ---------------------------------------------------------------------------------------------
 // 1x128 activations.  A 128-element group (256 bytes of bf16) is spread over the 16 lanes of a DPP row,
 // 8 elements per lane, so its max-abs is 4 row rotations.  Lane l of a wave works on K-block
 // 4 kq + l / 16 (kq = the workgroup's K-block quad) of 4 consecutive tokens, one token per load: each load
@@ -48,7 +85,7 @@ __device__ __forceinline__ uint32_t quant8_fp4(const u32x4 &v, double inv_s) {
 // 512 code bytes contiguously.  A workgroup (4 waves) covers 16 tokens x 4 K-blocks; its scales are 16
 // consecutive tokens of the K-block-major s_a layout for each of the 4 K-blocks.
 // ---------------------------------------------------------------------------------------------
-template <bool FP4>
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
     const int lane = threadIdx.x & 63;
@@ -77,12 +114,19 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
         amax = absmax2(amax, v[j].z);
         amax = absmax2(amax, v[j].w);
         amax = row16_max(amax);
-        const float sc = FP4 ? group_scale_fp4(amax) : group_scale(amax);
+        const float sc = FMT == kFmtFp4 ? group_scale_fp4(amax)
+                         : FMT == kFmtE5M6 ? group_scale_e5m6(amax) : group_scale(amax);
         const double inv = scale_reciprocal(sc);
         const int64_t m = row0 + j;
         if (m < M && kb_ok) {
-            if constexpr (FP4) {
+            if constexpr (FMT == kFmtFp4) {
                 *reinterpret_cast<uint32_t *>(q + m * (K / 2) + kb * 64 + i * 4) = quant8_fp4(v[j], inv);
+            } else if constexpr (FMT == kFmtE5M6) {
+                uint32_t *dst = reinterpret_cast<uint32_t *>(q + m * (K / 2 * 3) + kb * 192 + i * 12);
+                const uint3 o = quant8_e5m6(v[j], inv);
+                dst[0] = o.x;
+                dst[1] = o.y;
+                dst[2] = o.z;
             } else {
                 uint2 o;
                 o.x = quant4(v[j].x, v[j].y, inv);
@@ -467,7 +511,7 @@ hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8
                                   hipStream_t stream) {
     const int64_t KQ = (K / 128 + 3) / 4;
     const int64_t blocks = ((M + 15) / 16) * KQ;  // 1-D grid: K-block quad fastest, 16 tokens per workgroup
-    quant_act_1x128_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    quant_act_1x128_kernel<kFmtFp8><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
     return hipGetLastError();
 }
 
@@ -475,7 +519,15 @@ hipError_t launch_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, u
                                       hipStream_t stream) {
     const int64_t KQ = (K / 128 + 3) / 4;
     const int64_t blocks = ((M + 15) / 16) * KQ;
-    quant_act_1x128_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    quant_act_1x128_kernel<kFmtFp4><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s,
+                                       hipStream_t stream) {
+    const int64_t KQ = (K / 128 + 3) / 4;
+    const int64_t blocks = ((M + 15) / 16) * KQ;
+    quant_act_1x128_kernel<kFmtE5M6><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s);
     return hipGetLastError();
 }
 

@@ -85,6 +85,20 @@ int fp8q_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, fl
 int fp8q_quant_act_fp4_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
 int fp8q_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
 
+/* E5M6 activation quantization (page "The Definitive Information To Deepseek",
+ * the customized E5M6 format for certain activations; page "DeepSeek starts
+ * updating frequently", the TileKernels conversion to FP8, FP4 or E5M6).  The
+ * pages give the name only; this library reads E5M6 as sign, 5 exponent bits
+ * (bias 15), 6 mantissa bits, subnormals m * 2^-20, exponent 31 reserved
+ * (largest finite 65024), in the 1x128 activation groups:
+ *   x  : bf16 [M, K]            (input)
+ *   q  : [M, 3K/2] bytes        (output: 12-bit codes as a little-endian bit
+ *        stream, element j at bits 12j..12j+11 of its row)
+ *   s  : fp32 [K/128][M]        (output; s = fl32(amax / 65024))
+ * code = E5M6_RNE_saturating(fl32(x / s)), sign kept (-0 -> 0x800).
+ * Requires M >= 0, K % 128 == 0, 16-byte aligned pointers. */
+int fp8q_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, void *stream);
+
 /* Per-channel FP8 weight quantization (page "DeepSeek starts updating
  * frequently", the list of TileKernels features: per-token, per-block and
  * per-channel modes).  This library reads the per-channel mode as one scale

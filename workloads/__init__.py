@@ -167,6 +167,13 @@ def fp4(M=4096, N=18432, K=7168):
     return d
 
 
+def e5m6(M=4096, K=7168):
+    """The up projection's input (same recipe and seed as the up workload's A), for E5M6."""
+    d = dual(M, K)
+    d["name"] = "e5m6"
+    return d
+
+
 def per_channel(N=18432, K=7168):
     """The up projection's weight (same recipe and seed as the up workload), for per-channel FP8."""
     w = normal_bf16(SEEDS["up"], T_W, (N, K), 0.02)
@@ -174,4 +181,4 @@ def per_channel(N=18432, K=7168):
 
 
 WORKLOADS = {"tiny": tiny, "up": dense_up, "down": dense_down, "moe": moe, "decode": decode, "dequant": dequant,
-             "dual": dual, "fp4": fp4, "per_channel": per_channel}
+             "dual": dual, "fp4": fp4, "per_channel": per_channel, "e5m6": e5m6}
