@@ -256,6 +256,36 @@ class Workload:
                 ev[1].record()
 
 
+def measured_copy_gbs(mib: int = 1024, reps: int = 5) -> float:
+    """Device-to-device copy bandwidth (bytes read + written per second) of a plain torch copy over `mib` MiB,
+    the best of `reps` runs: the practical streaming rate of this GPU, beside the datasheet's 8 TB/s."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return 2 * (mib << 20) / (best * 1e-3) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wk: Workload, target_s: float = 12.0):
     """Time the CPU oracle (as it stands) on a bounded sample of the same workload: the 1x128 quantization
     of `rows` activation rows, the 128x128 quantization of the weight blocks those rows need, and the
@@ -569,6 +599,10 @@ def main():
         roof = {"kernel": gname, "bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
     roof["algorithmic_bytes"] = int(gwork["bytes"])
+    copy_gbs = measured_copy_gbs()
+    roof["measured_copy_GBs"] = round(copy_gbs, 1)
+    if roof["bound"] == "hbm":
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
 
     dq = args.workload in BANDWIDTH_METRICS
     out = {
@@ -598,6 +632,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wk)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(out), flush=True)
 
 
