@@ -117,15 +117,20 @@ class Workload:
             ab = 2 * M * K + M * K // 2 + 4 * (K // 128) * M
             wbytes = 2 * N * K + N * K // 2 + 4 * (N // 128) * (K // 128)
             self.bytes = ab + wbytes
-            self.kernels = [("quant_act_fp4_1x128", lambda: fq.fp8q_quant_act_fp4_1x128(self.a), {"bytes": ab}),
-                            ("quant_w_fp4_128x128", lambda: fq.fp8q_quant_w_fp4_128x128(self.w), {"bytes": wbytes})]
+            self.qa, self.sa = fq.fp8q_quant_act_fp4_1x128(self.a)      # output buffers, reused every step
+            self.qw, self.sw = fq.fp8q_quant_w_fp4_128x128(self.w)
+            self.kernels = [("quant_act_fp4_1x128", lambda: fq.fp8q_quant_act_fp4_1x128(self.a, self.qa, self.sa),
+                             {"bytes": ab}),
+                            ("quant_w_fp4_128x128", lambda: fq.fp8q_quant_w_fp4_128x128(self.w, self.qw, self.sw),
+                             {"bytes": wbytes})]
             torch.cuda.synchronize()
             return
         if name == "e5m6":
             self.a = bf16(d["a"])
             self.flops = 0.0
             self.bytes = 2 * M * K + M * K // 2 * 3 + 4 * (K // 128) * M
-            self.kernels = [("quant_act_e5m6_1x128", lambda: fq.fp8q_quant_act_e5m6_1x128(self.a),
+            self.qa, self.sa = fq.fp8q_quant_act_e5m6_1x128(self.a)
+            self.kernels = [("quant_act_e5m6_1x128", lambda: fq.fp8q_quant_act_e5m6_1x128(self.a, self.qa, self.sa),
                              {"bytes": self.bytes})]
             torch.cuda.synchronize()
             return
@@ -133,7 +138,8 @@ class Workload:
             self.w = bf16(d["w"])
             self.flops = 0.0
             self.bytes = 3 * N * K + 4 * N
-            self.kernels = [("quant_w_per_channel", lambda: fq.fp8q_quant_w_per_channel(self.w),
+            self.qw, self.sw = fq.fp8q_quant_w_per_channel(self.w)
+            self.kernels = [("quant_w_per_channel", lambda: fq.fp8q_quant_w_per_channel(self.w, self.qw, self.sw),
                              {"bytes": self.bytes})]
             torch.cuda.synchronize()
             return
@@ -141,7 +147,9 @@ class Workload:
             self.a = bf16(d["a"])
             self.flops = 0.0
             self.bytes = 4 * M * K + 4 * (K // 128) * M + 4 * (M // 128) * K
-            self.kernels = [("quant_act_dual", lambda: fq.fp8q_quant_act_dual(self.a), {"bytes": self.bytes})]
+            self.outs = fq.fp8q_quant_act_dual(self.a)
+            self.kernels = [("quant_act_dual", lambda: fq.fp8q_quant_act_dual(self.a, *self.outs),
+                             {"bytes": self.bytes})]
             torch.cuda.synchronize()
             return
         if name == "dequant":

@@ -196,17 +196,22 @@ def fp8q_quant_w_per_channel(w: torch.Tensor, q: torch.Tensor | None = None, s: 
     return q, s
 
 
-def fp8q_quant_act_dual(x: torch.Tensor, stream=None):
+def fp8q_quant_act_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None, stream=None):
     """Forward and backward FP8 copies of a Linear input in one pass.  ``x`` bf16 [M, K] (M, K multiples of
     128) -> ``(q uint8 [M, K], s float32 [K/128, M], qt uint8 [K, M], st float32 [M/128, K])``: the 1x128
-    quantization of x and of x^T (per channel, per 128 tokens)."""
+    quantization of x and of x^T (per channel, per 128 tokens).  Outputs not given are allocated."""
     _need(x, "x", _BF16, 2)
     M, K = x.shape
     dev = x.device
-    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    s = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
-    qt = torch.empty((K, M), dtype=torch.uint8, device=dev)
-    st = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((K // 128, M), dtype=torch.float32, device=dev) if s is None else s
+    qt = torch.empty((K, M), dtype=torch.uint8, device=dev) if qt is None else qt
+    st = torch.empty((M // 128, K), dtype=torch.float32, device=dev) if st is None else st
+    for t, name, dt, n in ((q, "q", torch.uint8, M * K), (s, "s", torch.float32, (K // 128) * M),
+                           (qt, "qt", torch.uint8, M * K), (st, "st", torch.float32, (M // 128) * K)):
+        _need(t, name, (dt,))
+        if t.numel() != n:
+            raise ValueError(f"{name} has the wrong size")
     _check(load_library().fp8q_quant_act_dual(_ptr(x), M, K, _ptr(q), _ptr(s), _ptr(qt), _ptr(st),
                                               _stream_ptr(stream)), "fp8q_quant_act_dual")
     return q, s, qt, st
