@@ -168,3 +168,35 @@ def test_dual_copies_past_4gib():
         oqt, ost = oracle.quant_act_backward_copy(host(x[r]))
         assert np.array_equal(host(qt[:, r].contiguous()), oqt), f"token block {mb}"
         assert np.array_equal(host(st[mb:mb + 1]).view(np.uint32), ost.view(np.uint32)), f"token block {mb}"
+
+
+def test_fp4_quant_past_4gib():
+    """FP4 in the 1x128 and 128x128 groups over a bf16 input of 8.0 GiB (codes: 2.0 GiB)."""
+    x = bf16_matrix(BIG, 116)
+    say(f"large: fp4 quant [{BIG}, {K}]")
+    q, s = fq.fp8q_quant_act_fp4_1x128(x)
+    rows = np.union1d(boundary_rows(2 * K, BIG), boundary_rows(K // 2, BIG))
+    ri = torch.from_numpy(rows).cuda()
+    oq, os_ = oracle.quant_act_fp4_1x128(host(x[ri]))
+    assert np.array_equal(host(q[ri]), oq)
+    assert np.array_equal(host(s[:, ri]).view(np.uint32), os_.view(np.uint32))
+    del q, s
+    q, s = fq.fp8q_quant_w_fp4_128x128(x)
+    for nb in np.unique(rows // 128):
+        r = slice(128 * nb, 128 * nb + 128)
+        oq, os_ = oracle.quant_w_fp4_128x128(host(x[r]))
+        assert np.array_equal(host(q[r]), oq), f"block {nb}"
+        assert np.array_equal(host(s[nb:nb + 1]).view(np.uint32), os_.view(np.uint32)), f"block {nb}"
+
+
+def test_e5m6_quant_past_4gib():
+    """E5M6 codes of [600064, 7168] (6.0 GiB of packed codes): rows on both sides of every 2^32-byte boundary
+    of the input and of the codes."""
+    x = bf16_matrix(BIG, 117)
+    say(f"large: e5m6 quant [{BIG}, {K}]")
+    q, s = fq.fp8q_quant_act_e5m6_1x128(x)
+    rows = np.union1d(boundary_rows(2 * K, BIG), boundary_rows(K // 2 * 3, BIG))
+    ri = torch.from_numpy(rows).cuda()
+    oq, os_ = oracle.quant_act_e5m6_1x128(host(x[ri]))
+    assert np.array_equal(host(q[ri]), oq)
+    assert np.array_equal(host(s[:, ri]).view(np.uint32), os_.view(np.uint32))
