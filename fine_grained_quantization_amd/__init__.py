@@ -13,6 +13,7 @@ this package is its Python binding.  Entry points (same names as the C functions
   fp8q_swiglu_bf16(x, y)                       the bf16 intermediate SiLU(x) * y alone
   fp8q_gemm_blockscaled(qa, sa, qw, sw)        -> C = A W^T, bf16 or fp32 [M, N]
   fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets)   MoE experts, one segment of rows each
+  fp8q_grouped_gemm_blockscaled_gather(q, s, row_token, qw, sw, offsets)   the same, reading token rows directly
   fp8q_dequant_w_128x128(q, s)                 E4M3 [N, K] + fp32 [N/128, K/128] -> bf16 [N, K]
   fp8q_moe_route_topk(logits, k)               top-k experts and the expert-sorted, 128-padded row layout
   fp8q_moe_gather_fp8(q, s, row_of, row_token, offsets)   quantized token rows in that layout (FP8 dispatch)
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     fp8q_dequant_w_128x128,
     fp8q_gemm_blockscaled,
     fp8q_grouped_gemm_blockscaled,
+    fp8q_grouped_gemm_blockscaled_gather,
     fp8q_moe_gather_fp8,
     fp8q_moe_route_capacity,
     fp8q_moe_route_topk,

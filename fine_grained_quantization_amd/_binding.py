@@ -45,13 +45,15 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I64, I64, I64, P]
         lib.fp8q_grouped_gemm_blockscaled.argtypes = [P, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_dequant_w_128x128.argtypes = [P, P, I64, I64, P, P]
+        lib.fp8q_grouped_gemm_blockscaled_gather.argtypes = [P, P, I64, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_moe_route_topk.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, P]
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
                   lib.fp8q_swiglu_bf16, lib.fp8q_quant_act_dual, lib.fp8q_quant_act_fp4_1x128,
                   lib.fp8q_quant_w_fp4_128x128, lib.fp8q_quant_w_per_channel, lib.fp8q_quant_act_e5m6_1x128,
                   lib.fp8q_gemm_blockscaled,
-                  lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
+                  lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_grouped_gemm_blockscaled_gather,
+                  lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
                   lib.fp8q_moe_gather_fp8):
             f.restype = ctypes.c_int
         lib.fp8q_moe_route_capacity.argtypes = [I64, I64, I64]
@@ -368,6 +370,35 @@ def fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, offsets, out_dtype=torch.bfloa
     _check(load_library().fp8q_grouped_gemm_blockscaled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(c), code,
                                                         _ptr(offsets), E, M, N, K, _stream_ptr(stream)),
            "fp8q_grouped_gemm_blockscaled")
+    return c
+
+
+def fp8q_grouped_gemm_blockscaled_gather(q, s, row_token, qw, sw, offsets, out_dtype=torch.bfloat16, c=None,
+                                         stream=None):
+    """Grouped GEMM reading each row's token through ``row_token`` (the FP8 dispatch folded into the GEMM).
+    ``q`` [T, K] token codes, ``s`` [K/128, T] token scales, ``row_token`` int32 device [M_total] (-1: empty
+    row), ``qw`` [E, N, K], ``sw`` [E, N/128, K/128], ``offsets`` int32 device [E+1] -> ``c`` [M_total, N]."""
+    _need(q, "q", _FP8, 2)
+    _need(qw, "qw", _FP8, 3)
+    _need(s, "s", (torch.float32,))
+    _need(sw, "sw", (torch.float32,))
+    _need(row_token, "row_token", (torch.int32,), 1)
+    _need(offsets, "offsets", (torch.int32,), 1)
+    T, K = q.shape
+    E, N, K2 = qw.shape
+    M = row_token.numel()
+    if K2 != K or s.numel() != (K // 128) * T or sw.numel() != E * (N // 128) * (K // 128) or \
+            offsets.numel() != E + 1:
+        raise ValueError("inconsistent grouped GEMM operand shapes")
+    code = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=qw.device)
+    _need(c, "c", (out_dtype,))
+    if c.numel() != M * N:
+        raise ValueError("c has the wrong size")
+    _check(load_library().fp8q_grouped_gemm_blockscaled_gather(
+        _ptr(q), _ptr(s), T, _ptr(row_token), _ptr(qw), _ptr(sw), _ptr(c), code, _ptr(offsets), E, M, N, K,
+        _stream_ptr(stream)), "fp8q_grouped_gemm_blockscaled_gather")
     return c
 
 

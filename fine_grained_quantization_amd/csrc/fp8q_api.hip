@@ -208,6 +208,27 @@ int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint
                                                         M_total, N, K, static_cast<hipStream_t>(stream)));
 }
 
+int fp8q_grouped_gemm_blockscaled_gather(const uint8_t *q, const float *s, int64_t T, const int32_t *row_token,
+                                         const uint8_t *qw, const float *sw, void *c, int out_dtype,
+                                         const int32_t *off, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                         void *stream) {
+    if (E < 1 || M_total < 0 || M_total % 128 || N < 0 || K < 128 || K > kMaxK || N % 128 || K % 128 || T < 0)
+        return FP8Q_ERR_SHAPE;
+    if (M_total > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;           // offsets are int32
+    if (T > 0 && T > (int64_t)0x7FFFFFFF / K) return FP8Q_ERR_SHAPE;  // token offsets are 32-bit
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
+    if (M_total == 0 || N == 0) return FP8Q_OK;
+    if (!row_token || !qw || !sw || !c || !off || (T > 0 && (!q || !s))) return FP8Q_ERR_NULL;
+    if (!aligned16(qw) || !aligned16(sw) || !aligned16(c) || !aligned4(off) || !aligned4(row_token) ||
+        (T > 0 && (!aligned16(q) || !aligned4(s))))
+        return FP8Q_ERR_ALIGN;
+    if (fp8q::gemm_blocks(M_total, N) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(fp8q::launch_grouped_gemm_gather(q, s, T, row_token, qw, sw, c, out_dtype == FP8Q_OUT_BF16, off, E,
+                                                   M_total, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int64_t fp8q_moe_route_capacity(int64_t T, int64_t E, int64_t k) {
     if (T < 0 || E < 1 || E > fp8q::kMoeMaxExperts || k < 1 || k > E || k > fp8q::kMoeMaxK) return -1;
     if (T > (int64_t(1) << 40)) return -1;

@@ -288,6 +288,37 @@ struct TileLoader {
             wvoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
         }
     }
+    // The same tile when its A rows are token rows picked through a row -> token map (the FP8 dispatch folded
+    // into the grouped GEMM): A row r of the tile is token rt[r] of q [T, K] (rows past `rows`, and rows whose
+    // token is negative or >= T, read zeros), and its scale is s_tok[kb * T + token].
+    __device__ __forceinline__ void init_gather(const uint8_t *q, int64_t T, const int32_t *rt, int64_t rows,
+                                                const uint8_t *w_rows, uint64_t w_bytes, int64_t K, int wave,
+                                                int lane, const float *s_tok, const float *sw_mat, int64_t NB,
+                                                int64_t nb0) {
+        ra = make_rsrc(q, (uint64_t)T * (uint64_t)K);
+        rw = make_rsrc(w_rows, w_bytes);
+        const int64_t KB = K >> 7;
+        rsw = make_rsrc(sw_mat, (uint64_t)NB * (uint64_t)KB * 4);
+        const int64_t nb = nb0 + lane < NB - 1 ? nb0 + lane : NB - 1;
+        int64_t sc_tok = -1;
+        if (wave < 4 && wave * 64 + lane < rows) sc_tok = rt[wave * 64 + lane];
+        scvoff = wave < 4 ? (sc_tok >= 0 && sc_tok < T ? (int)(sc_tok * 4) : kOutOfRange)
+                          : (lane < 3 ? (int)(nb * KB * 4) : kOutOfRange);
+        sa_tile = s_tok;
+        sa_bytes = (uint64_t)T * 4;
+        M = T;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int r = wave * 32 + j * 8 + (lane >> 3);
+            const int64_t tok = r < rows ? rt[r] : -1;
+            avoff[j] = tok >= 0 && tok < T ? (int)(tok * K) + (((lane & 7) ^ swzf(r)) << 4) : kOutOfRange;
+        }
+#pragma unroll
+        for (int j = 0; j < kWPerWave; j++) {
+            const int r = (wave + 8 * j) * 8 + (lane >> 3);
+            wvoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
+        }
+    }
     // Copies K-block kb (or, for koff == kOutOfRange, nothing) into `stage`; the scales of K-block ks
     // (kb, clamped to the last block) come along, one dword per lane from in-bounds addresses.
     __device__ __forceinline__ void issue(uint8_t *stage, int koff, int64_t ks, int wave) const {
@@ -400,12 +431,15 @@ __device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restric
 // WAVES_N along M (64 tokens each) x WAVES_N along N (16 NSUB weight rows each).  WAVES_N = 2 is the 256-row
 // tile; WAVES_N = 4 (NSUB = 4) is the 128 x 256 tile for grouped segments with 128 rows left.  W / SW are the
 // weight matrix and its scales (an expert's, in the grouped case), and rows >= mend are not stored.
-// stage0 / stage1 are the workgroup's two LDS stages, each at least TileLoader<BN>::kStageBytes.
-template <bool OUT_BF16, int NSUB, int WAVES_N>
+// stage0 / stage1 are the workgroup's two LDS stages, each at least TileLoader<BN>::kStageBytes.  With GATHER,
+// qa / sa are token codes [T, K] and token scales [K/128][T], and output row r's activation row is token
+// rtok[r] (the dispatch gather folded into the GEMM).
+template <bool OUT_BF16, int NSUB, int WAVES_N, bool GATHER = false>
 __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const uint8_t *__restrict__ qa,
                                         const float *__restrict__ sa, const uint8_t *__restrict__ W,
                                         const float *__restrict__ SW, void *__restrict__ c, int64_t M, int64_t N,
-                                        int64_t K, int64_t m0, int64_t mend, int64_t n0) {
+                                        int64_t K, int64_t m0, int64_t mend, int64_t n0,
+                                        const int32_t *__restrict__ rtok = nullptr, int64_t T = 0) {
     constexpr int WM_WAVES = 8 / WAVES_N;
     constexpr int BN = 16 * NSUB * WAVES_N;
     constexpr int WN = 16 * NSUB;  // weight rows per wave
@@ -426,8 +460,12 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
     const int nbB = nbA + 1 < 2 ? nbA + 1 : 2;
     const int nib = (int)((128 * (nw0 / 128 + 1) - nw0) / 16);
     TileLoader<BN> ld;
-    ld.init(qa + m0 * K, (uint64_t)(mend - m0) * (uint64_t)K, W + n0 * K, (uint64_t)(N - n0) * (uint64_t)K, K,
-            wave, lane, sa + m0, mend - m0, M, SW, N / 128, nb0);
+    if constexpr (GATHER)
+        ld.init_gather(qa, T, rtok + m0, mend - m0, W + n0 * K, (uint64_t)(N - n0) * (uint64_t)K, K, wave, lane,
+                       sa, SW, N / 128, nb0);
+    else
+        ld.init(qa + m0 * K, (uint64_t)(mend - m0) * (uint64_t)K, W + n0 * K, (uint64_t)(N - n0) * (uint64_t)K, K,
+                wave, lane, sa + m0, mend - m0, M, SW, N / 128, nb0);
 
     v4f acc[NSUB][4];
 #pragma unroll
@@ -540,7 +578,7 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
 // which are dispatched as the CUs finish their last main tiles and so fill the otherwise idle part of the
 // last round.  Grouped (NSUB = 8): one 256 x 256 tile per workgroup, or 128 x 256 where a segment has
 // only 128 rows left.
-template <bool OUT_BF16, bool GROUPED, int NSUB, int NSUB_TAIL>
+template <bool OUT_BF16, bool GROUPED, int NSUB, int NSUB_TAIL, bool GATHER = false>
 __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__restrict__ qa,
                                                              const float *__restrict__ sa,
                                                              const uint8_t *__restrict__ qw,
@@ -548,7 +586,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
                                                              int64_t M, int64_t N, int64_t K,
                                                              const int32_t *__restrict__ off, int64_t E,
                                                              int64_t n_mtiles, int64_t n_ntiles, int64_t main_tiles,
-                                                             int64_t n_tail, int64_t n_ntiles_tail) {
+                                                             int64_t n_tail, int64_t n_ntiles_tail,
+                                                             const int32_t *__restrict__ rtok = nullptr,
+                                                             int64_t T = 0) {
     constexpr int kMain = TileLoader<32 * NSUB>::kStageBytes;
     constexpr int kTail = TileLoader<32 * (NSUB_TAIL ? NSUB_TAIL : NSUB)>::kStageBytes;
     constexpr int kStageBytes = kMain > kTail ? kMain : kTail;
@@ -568,9 +608,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bs_256_kernel(const uint8_t *__re
         const uint8_t *W = qw + e * N * K;
         const float *SW = sw + e * (N / 128) * (K >> 7);
         if (mend - m0 <= 128)  // a segment's last 128 rows: the 128 x 256 layout does no work on absent rows
-            bs_tile<OUT_BF16, 4, 4>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0);
+            bs_tile<OUT_BF16, 4, 4, GATHER>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0, rtok, T);
         else
-            bs_tile<OUT_BF16, NSUB, 2>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0);
+            bs_tile<OUT_BF16, NSUB, 2, GATHER>(stage0, stage1, qa, sa, W, SW, c, M, N, K, m0, mend, n0, rtok, T);
         return;
     }
     // Dense: the main tiles, then (NSUB_TAIL != 0) the narrower tail tiles, as one sequence of tiles in XCD
@@ -701,6 +741,20 @@ hipError_t launch_256_grouped(const uint8_t *qa, const float *sa, const uint8_t 
     const int64_t blocks = (n_mtiles * n_ntiles + 255) / 256 * 256;
     gemm_bs_256_kernel<OUT_BF16, true, 8, 0><<<dim3((unsigned)blocks), 512, 0, stream>>>(
         qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0);
+    return hipGetLastError();
+}
+
+// The grouped GEMM reading its activation rows through the row -> token map (same tiles and order).
+template <bool OUT_BF16>
+hipError_t launch_256_grouped_gather(const uint8_t *q, const float *s, int64_t T, const int32_t *rtok,
+                                     const uint8_t *qw, const float *sw, void *c, int64_t M, int64_t N, int64_t K,
+                                     const int32_t *off, int64_t E, hipStream_t stream) {
+    constexpr int64_t BN = 256;
+    const int64_t n_ntiles = (N + BN - 1) / BN;
+    const int64_t n_mtiles = M / kBig + (E + 1) / 2;
+    const int64_t blocks = (n_mtiles * n_ntiles + 255) / 256 * 256;
+    gemm_bs_256_kernel<OUT_BF16, true, 8, 0, true><<<dim3((unsigned)blocks), 512, 0, stream>>>(
+        q, s, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0, rtok, T);
     return hipGetLastError();
 }
 
@@ -938,6 +992,14 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, c
                                            int64_t N, int64_t K, hipStream_t stream) {
     return out_bf16 ? launch_256_grouped<true>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream)
                     : launch_256_grouped<false>(qa, sa, qw, sw, c, M_total, N, K, off, E, stream);
+}
+
+hipError_t launch_grouped_gemm_gather(const uint8_t *q, const float *s, int64_t T, const int32_t *row_token,
+                                      const uint8_t *qw, const float *sw, void *c, bool out_bf16,
+                                      const int32_t *off, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                      hipStream_t stream) {
+    return out_bf16 ? launch_256_grouped_gather<true>(q, s, T, row_token, qw, sw, c, M_total, N, K, off, E, stream)
+                    : launch_256_grouped_gather<false>(q, s, T, row_token, qw, sw, c, M_total, N, K, off, E, stream);
 }
 
 }  // namespace fp8q

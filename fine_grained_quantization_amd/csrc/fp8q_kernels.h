@@ -30,6 +30,10 @@ hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uin
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
                                            void *c, bool out_bf16, const int32_t *off, int64_t E, int64_t M_total,
                                            int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_grouped_gemm_gather(const uint8_t *q, const float *s, int64_t T, const int32_t *row_token,
+                                      const uint8_t *qw, const float *sw, void *c, bool out_bf16,
+                                      const int32_t *off, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                      hipStream_t stream);
 // MoE routing: experts at most kMoeMaxExperts, k at most kMoeMaxK.
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeMaxK = 16;

@@ -203,6 +203,24 @@ int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint
                                   int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
                                   int64_t K, void *stream);
 
+/* The grouped GEMM with the FP8 dispatch folded in (page "DeepSeek starts
+ * updating frequently": DeepEP V2 dispatches tokens in FP8 to the experts'
+ * GEMMs).  Instead of a gathered A, the GEMM reads each row's token directly:
+ * row r of the expert-sorted layout is token row_token[r] of the quantized
+ * tokens, exactly as if fp8q_moe_gather_fp8 had copied it there first (the
+ * results are identical):
+ *   q   : E4M3 [T, K] token codes,  s : fp32 [K/128][T] token scales
+ *   row_token : DEVICE int32 [M_total]; a value outside [0, T) (the routing's
+ *         -1) is an empty row: codes 0, scale 0, output exactly 0
+ *   qw, sw, off, c, out_dtype, E, M_total, N, K : as fp8q_grouped_gemm_blockscaled
+ * Requires what fp8q_grouped_gemm_blockscaled requires, plus T >= 0 and
+ * T * K < 2^31; q and s may be null when T == 0.  The same guarantees hold
+ * for offsets that break the rules. */
+int fp8q_grouped_gemm_blockscaled_gather(const uint8_t *q, const float *s, int64_t T, const int32_t *row_token,
+                                         const uint8_t *qw, const float *sw, void *c, int out_dtype,
+                                         const int32_t *off, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                         void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fp8q_moe_route_workspace_bytes", "fp8q_moe_route_topk", "fp8q_moe_gather_fp8",
               "fp8q_swiglu_quant_act_1x128", "fp8q_swiglu_bf16", "fp8q_quant_act_dual",
               "fp8q_quant_act_fp4_1x128", "fp8q_quant_w_fp4_128x128", "fp8q_quant_w_per_channel",
-              "fp8q_quant_act_e5m6_1x128", "fp8q_status_string", "fp8q_version"):
+              "fp8q_quant_act_e5m6_1x128", "fp8q_grouped_gemm_blockscaled_gather", "fp8q_status_string", "fp8q_version"):
         assert n in names
 
 
@@ -92,6 +92,14 @@ def test_argument_validation_without_device(lib):
     assert lib.fp8q_quant_act_fp4_1x128(None, 0, 128, None, None, None) == 0
     assert lib.fp8q_quant_act_fp4_1x128(A, 4, 128, None, B, None) == -1
     assert lib.fp8q_quant_w_fp4_128x128(A, 128, 128, MIS, B, None) == -3
+    # grouped GEMM reading token rows through row_token
+    gg = lib.fp8q_grouped_gemm_blockscaled_gather
+    assert gg(A, A, 4, B, A, A, A, 0, B, 2, 100, 128, 128, None) == -2          # M_total not a multiple of 128
+    assert gg(A, A, -1, B, A, A, A, 0, B, 2, 128, 128, 128, None) == -2         # negative T
+    assert gg(A, A, 1 << 30, B, A, A, A, 0, B, 2, 128, 128, 128, None) == -2    # T * K past 2^31
+    assert gg(A, A, 4, B, A, A, A, 0, B, 2, 0, 128, 128, None) == 0             # no rows
+    assert gg(A, A, 4, None, A, A, A, 0, B, 2, 128, 128, 128, None) == -1       # no row map
+    assert gg(A, A, 4, B, A, A, A, 7, B, 2, 128, 128, 128, None) == -4          # bad out dtype
     # E5M6 activations
     assert lib.fp8q_quant_act_e5m6_1x128(A, 4, 100, B, B, None) == -2
     assert lib.fp8q_quant_act_e5m6_1x128(None, 0, 128, None, None, None) == 0

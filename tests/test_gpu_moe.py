@@ -8,7 +8,8 @@ import torch
 import fine_grained_quantization_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import assert_gemm_within_bound, bf16_dev, f32_dev, gemm_out_to_f64, host, say, u8_dev
+from gpu_util import (assert_gemm_within_bound, bf16_bits_to_f64, bf16_dev, f32_dev, gemm_out_to_f64, host, say,
+                      u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +142,86 @@ def test_full_dispatch_path_of_the_moe_layer():
     assert np.all(ch[empty] == 0.0)
     assert np.all(np.isnan(ch[used:]))
     say(f"  grouped GEMM max err/bound {ratio:.3g}")
+
+
+def fused_and_separate(q, s, logits, k, qw, sw, out, rows=None):
+    """The grouped GEMM on gathered rows, and the gather-fused grouped GEMM on the token rows, both into
+    buffers pre-filled with NaN; returns (separate, fused, routing)."""
+    T, K = q.shape
+    E = logits.shape[1]
+    cap = oracle.moe_route_capacity(T, E, k) if rows is None else rows
+    r = oracle.moe_route_topk(logits, k, rows=cap)
+    N = qw.shape[1]
+    off = torch.from_numpy(r.offsets).cuda()
+    rt = torch.from_numpy(r.row_token).cuda()
+    qd, sd = u8_dev(q), f32_dev(s)
+    qa = torch.zeros((cap, K), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((K // 128, cap), dtype=torch.float32, device="cuda")
+    fq.fp8q_moe_gather_fp8(qd, sd, torch.from_numpy(r.row_of.reshape(T, k)).cuda(), rt, off, qa, sa)
+    c1 = torch.full((cap, N), float("nan"), dtype=out, device="cuda")
+    c2 = torch.full((cap, N), float("nan"), dtype=out, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, off, out_dtype=out, c=c1)
+    fq.fp8q_grouped_gemm_blockscaled_gather(qd, sd, rt, qw, sw, off, out_dtype=out, c=c2)
+    return host(c1), host(c2), r
+
+
+def same_bits(a, b):
+    return np.array_equal(a.view(np.uint16 if a.dtype == np.uint16 else np.uint32),
+                          b.view(np.uint16 if b.dtype == np.uint16 else np.uint32))
+
+
+@pytest.mark.parametrize("T,K,N,E,k,out", [(300, 512, 256, 64, 8, torch.bfloat16), (5, 128, 384, 4, 2, torch.float32),
+                                           (0, 256, 128, 8, 2, torch.bfloat16), (1000, 1024, 512, 16, 4, torch.float32)])
+def test_gather_fused_grouped_gemm_matches_gather_then_gemm(T, K, N, E, k, out):
+    """Bit-identical to gathering the rows first, padding rows exactly 0, rows past the layout untouched, and
+    within the GEMM bound of the oracle on every row."""
+    g = np.random.default_rng([23, T, K, N])
+    q = g.integers(0, 254, size=(T, K)).astype(np.uint8)
+    q[q >= 0x7F] += 1                                     # finite codes only
+    s = g.uniform(1e-4, 1e-2, size=(K // 128, T)).astype(np.float32)
+    w = wl.bf16_bits((g.standard_normal((E * N, K)) * 0.02).astype(np.float32))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(w).view(E, N, K))
+    say(f"gather-fused grouped: T={T} K={K} N={N} E={E} k={k} {out}")
+    c1, c2, r = fused_and_separate(q, s, logits_of("normal", T, E, 7), k, qw, sw, out)
+    assert same_bits(c1, c2)
+    used = r.M
+    f = bf16_bits_to_f64(c2) if out == torch.bfloat16 else c2.astype(np.float64)
+    assert np.all(np.isnan(f[used:]))
+    empty = np.nonzero(r.row_token[:used] < 0)[0]
+    assert np.all(f[empty] == 0.0)
+    if used:
+        oqa, osa = oracle.moe_gather_fp8(q, s, r.row_token[:used])
+        C, B = oracle.grouped_gemm_blockscaled(oqa, osa, host(qw), host(sw), r.offsets)
+        assert_gemm_within_bound(f[:used], C, B, out == torch.bfloat16, "gather-fused grouped")
+
+
+def test_gather_fused_tokens_out_of_range_read_as_empty_rows():
+    """A row whose token is >= T (as well as -1) gives an exactly zero output row."""
+    T, K, N, E = 64, 256, 256, 2
+    g = np.random.default_rng(24)
+    q = g.integers(0, 0x7E, size=(T, K)).astype(np.uint8)
+    s = g.uniform(1e-3, 1e-2, size=(K // 128, T)).astype(np.float32)
+    w = wl.bf16_bits((g.standard_normal((E * N, K)) * 0.02).astype(np.float32))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(w).view(E, N, K))
+    rt = np.arange(256, dtype=np.int32) % (T + 40)          # tokens T .. T+39 are out of range
+    rt[::7] = -1
+    off = torch.tensor([0, 128, 256], dtype=torch.int32, device="cuda")
+    c = fq.fp8q_grouped_gemm_blockscaled_gather(u8_dev(q), f32_dev(s), torch.from_numpy(rt).cuda(), qw, sw, off,
+                                                out_dtype=torch.float32)
+    c = host(c)
+    bad = (rt < 0) | (rt >= T)
+    assert np.all(c[bad] == 0.0) and np.all(np.abs(c[~bad]).sum(axis=1) > 0)
+
+
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
+def test_gather_fused_moe_layer(out):
+    """The MoE layer's dispatch (8192 tokens x 7168, top-8 of 64, 64 experts x [2048, 7168]) through the
+    gather-fused grouped GEMM: bit-identical to gather + grouped GEMM over the whole routing capacity."""
+    d = wl.moe()
+    T, E, k, K = d["T"], d["E"], d["topk"], d["K"]
+    say(f"gather-fused grouped: moe layer {out}")
+    q, s = oracle.quant_act_1x128(d["tokens"])
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(d["w"]))
+    c1, c2, r = fused_and_separate(q, s, d["logits"], k, qw, sw, out)
+    assert same_bits(c1, c2)
+    say(f"  bit-identical over {r.M} rows")
