@@ -209,6 +209,27 @@ def test_grouped_offsets_outside_the_rules():
     assert_gemm_within_bound(gemm_out_to_f64(c), C, B, False, "offset past M_total")
 
 
+def test_grouped_gather_with_offsets_outside_the_rules():
+    """The gather-reading grouped GEMM under the same broken offsets (short, past M_total, decreasing), with
+    the identity row map over 1024 token rows: bit-identical to the grouped GEMM on the same rows, including
+    the rows each leaves untouched."""
+    K, N, M = 512, 256, 1024
+    g = np.random.default_rng(6)
+    ab = wl.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    wb = wl.bf16_bits((g.standard_normal((2, N, K)) * 0.02).astype(np.float32))
+    qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(ab))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(wb))
+    rt = torch.arange(M, dtype=torch.int32, device="cuda")
+    for offs in ([0, 384, 640], [0, 256, 2048], [0, 512, 256], [0, 0, 0]):
+        say(f"grouped gemm, gather form: offsets {offs}")
+        off = torch.tensor(offs, dtype=torch.int32, device="cuda")
+        c1 = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+        c2 = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+        fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, off, out_dtype=torch.float32, c=c1)
+        fq.fp8q_grouped_gemm_blockscaled_gather(qa, sa, rt, qw, sw, off, out_dtype=torch.float32, c=c2)
+        assert np.array_equal(host(c1).view(np.uint32), host(c2).view(np.uint32)), offs
+
+
 def test_grouped_full_moe_sampled():
     """The full MoE layer: 8192 tokens, top-8 of 64 experts, expert weights [2048, 7168]; sampled rows
     from every expert segment (first, last routed row and a random one), all 2048 columns."""
