@@ -53,15 +53,17 @@ constexpr double kInv65024 = 1.0 / 65024.0;
 // least 2^-8 of an fp32 unit from any midpoint, far beyond the double product's error.
 __device__ __forceinline__ float group_scale_e5m6(float amax) { return (float)((double)amax * kInv65024); }
 
-// E5M6 code of an fp32 value v with |v| <= 65024 (1 + 2^-23): normal results round the fp32 pattern to 6
-// mantissa bits (nearest even, a carry runs into the exponent) and rebias 127 -> 15; below 2^-14 the code
-// is the subnormal count v * 2^20 (exact) rounded to nearest even.  Checked on the CPU against the oracle's
-// encoder on every 7th fp32 pattern up to 65024 (1 + 2^-23), both signs, and every midpoint.
+// E5M6 code of an fp32 value v with |v| <= 65024 (1 + 2^-23).  Normal results (|v| >= 2^-14) round the fp32
+// pattern to 6 mantissa bits, nearest even, with the rebias 127 -> 15 folded into the same add (a carry runs
+// into the exponent).  Below 2^-14 the code is the number of 2^-20 steps: |v| + 8 lands in [8, 16), whose
+// spacing is 2^-20, so the fp32 add rounds |v| to that grid (nearest even) and the pattern difference from
+// 8.0 is the count (64 being the smallest normal code).  Checked on the CPU against the oracle's encoder on
+// every 7th fp32 pattern up to 65024 (1 + 2^-23), both signs, and every midpoint.
 __device__ __forceinline__ uint32_t e5m6_code(float v) {
     const uint32_t b = __float_as_uint(v);
     const uint32_t a = b & 0x7FFFFFFFu;
-    const uint32_t normal = min(((a + 0xFFFFu + ((a >> 17) & 1u)) >> 17) - (112u << 6), 0x7BFu);
-    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1p20f);
+    const uint32_t normal = min((a + (0xFFFFu - (112u << 23)) + ((a >> 17) & 1u)) >> 17, 0x7BFu);
+    const uint32_t sub = __float_as_uint(__uint_as_float(a) + 8.0f) - 0x41000000u;
     return ((b >> 20) & 0x800u) | (a >= 0x38800000u ? normal : sub);
 }
 
