@@ -19,8 +19,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
- *     and contiguous, with base addresses aligned to 16 bytes.  The library
- *     never allocates, frees or synchronizes.
+ *     and contiguous, with base addresses aligned to 16 bytes unless an entry
+ *     point states a weaker rule.  The library never allocates, frees or
+ *     synchronizes.
  *   - bf16 tensors are passed as uint16_t bit patterns.  FP8 tensors are
  *     uint8_t OCP E4M3 codes (0x7F / 0xFF are NaN and never produced).
  *   - Scales are fp32.  Activation scales s_a have layout [K/128][M]
@@ -37,7 +38,8 @@
  *     host pointer passed as a device pointer) surface at the caller's
  *     synchronization, as for any HIP kernel.
  *   - Finite inputs are a precondition.  Shapes are int64_t.  M may be any
- *     value >= 0 (M == 0 launches nothing); K and N must be multiples of 128.
+ *     value >= 0 (M == 0 launches nothing); K and N must be multiples of 128
+ *     unless an entry point states otherwise.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
