@@ -292,6 +292,93 @@ def cpu_model() -> str:
     return "unknown"
 
 
+class ClockSampler:
+    """The GPU's graphics clocks while the steps run, from the device's metrics table (amdsmi), which the
+    firmware refreshes about once a second with the clock of each XCD averaged over that second.  A host
+    thread polls the table every `period_s` between start() and stop() and keeps each refresh once.  Reading
+    it needs no GPU work.  Where amdsmi is missing or refuses (no permission, no matching device), the record
+    says why and holds no windows."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+
+        self.period_s = period_s
+        self.windows: list[tuple[float, list[int]]] = []   # (host time first seen, per-XCD MHz)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._handle = self._match(amdsmi, amdsmi.amdsmi_get_processor_handles())
+            self._metrics = lambda: amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+            self._metrics()
+        except Exception as e:  # the benchmark runs on without the clock record
+            self._handle, self.error = None, f"{type(e).__name__}: {' '.join(str(e).split())}"
+
+    @staticmethod
+    def _match(amdsmi, handles):
+        """The amdsmi handle of torch's device 0: the only GPU, or the one whose PCI address matches."""
+        if len(handles) == 1:
+            return handles[0]
+        import torch
+
+        p = torch.cuda.get_device_properties(0)
+        want = (getattr(p, "pci_domain_id", None), getattr(p, "pci_bus_id", None),
+                getattr(p, "pci_device_id", None))
+        if None not in want:
+            for h in handles:
+                d, b, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(d, 16), int(b, 16), int(rest.split(".")[0], 16)) == want:
+                    return h
+        raise RuntimeError(f"{len(handles)} GPUs and none matched to torch's device 0")
+
+    def _run(self):
+        last = None
+        while not self._stop.is_set():
+            try:
+                m = self._metrics()
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {' '.join(str(e).split())}"
+                return
+            stamp = m.get("system_clock_counter")
+            xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)] \
+                if isinstance(m.get("current_gfxclks"), list) else []
+            if stamp != last and xcd:
+                self.windows.append((time.perf_counter(), xcd))
+                last = stamp
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=1.0)
+
+    def record(self, busy_from: float, busy_to: float, window_s: float = 1.05):
+        """Clocks over the refreshes whose whole averaging window (about a second before each) lies in
+        [busy_from, busy_to] (host perf_counter seconds): the mean over XCDs and windows, and the slowest and
+        fastest XCD."""
+        v = [x for t, x in self.windows if busy_from + window_s <= t <= busy_to]
+        out = {"source": "amdsmi metrics table, per-XCD GFX clock averaged over each ~1 s refresh",
+               "windows": len(v)}
+        if v:
+            flat = [c for x in v for c in x]
+            out.update(MHz_mean=round(float(np.mean(flat)), 1), MHz_min_xcd=min(flat), MHz_max_xcd=max(flat),
+                       xcds=len(v[0]))
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
 def cpu_baseline(wk: Workload, target_s: float = 12.0):
     """Time the CPU oracle (as it stands) on a bounded sample of the same workload: the 1x128 quantization
     of `rows` activation rows, the 128x128 quantization of the weight blocks those rows need, and the
@@ -512,7 +599,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="up", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
+    ap.add_argument("--settle-ms", type=float, default=2500.0,
                     help="before the warmup steps, repeat the step for this long (untimed) so that the GPU's "
                          "clocks reach their sustained state; the count is reported as settle_steps")
     ap.add_argument("--pmc-copy-mb", type=int, default=0,
@@ -539,6 +626,8 @@ def main():
         del src, dst
     # Settle: a few milliseconds of warmup leave the GPU below its sustained clock (measured: the up GEMM
     # runs at 568 us after 5 steps, 490 us after 100), so repeat the step, untimed, for settle_ms first.
+    clock = ClockSampler()
+    clock.start()
     settle_steps = 0
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
@@ -564,7 +653,9 @@ def main():
         wk.step([None] * (nk - 1) + [gemm_ev[s]])
     end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    wall1 = time.perf_counter()
+    wall = wall1 - wall0
+    clock.stop()
     ms_step = start.elapsed_time(end) / args.steps
     gemm_us = 1e3 * float(np.mean([he.elapsed_ms(a, b) for a, b in gemm_raw]))
     for a, b in gemm_raw:
@@ -612,6 +703,14 @@ def main():
     roof["measured_copy_GBs"] = round(copy_gbs, 1)
     if roof["bound"] == "hbm":
         roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
+    # The clock while the steps ran: the metrics windows that lie inside the settle phase and the timed
+    # region (the timed region alone is far shorter than one window).
+    clk = clock.record(t_settle, wall1)
+    if roof["bound"] == "mfma" and "MHz_mean" in clk:
+        # 256 CUs x 4 SIMDs x 2048 FP8 flop per clock (a 16x16x128 MFMA every 32 cycles)
+        at_clock = 256 * 8192 * clk["MHz_mean"] * 1e6 / 1e12
+        roof["peak_at_measured_clock"] = round(at_clock, 1)
+        roof["frac_at_measured_clock"] = round(roof["achieved"] / at_clock, 4)
 
     dq = args.workload in BANDWIDTH_METRICS
     out = {
@@ -635,6 +734,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
+        "gpu_clock": clk,
     }
     if args.workload == "moe":
         out["config"]["rows_used"] = wk.rows_used   # M is the routing capacity the buffers are sized to
