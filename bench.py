@@ -657,7 +657,7 @@ def main():
     wall = wall1 - wall0
     clock.stop()
     ms_step = start.elapsed_time(end) / args.steps
-    gemm_us = 1e3 * float(np.mean([he.elapsed_ms(a, b) for a, b in gemm_raw]))
+    gemm_all = [1e3 * he.elapsed_ms(a, b) for a, b in gemm_raw]
     for a, b in gemm_raw:
         he.destroy(a)
         he.destroy(b)
@@ -671,10 +671,12 @@ def main():
     kernels = {}
     for i, (kname, _, work) in enumerate(wk.kernels):  # (all event pairs are destroyed below)
         if i == nk - 1:
-            us = gemm_us  # measured in the timed region
+            each = gemm_all  # measured in the timed region
         else:
-            us = 1e3 * float(np.mean([he.elapsed_ms(*raw[s][i]) for s in range(args.steps)]))
-        info = {"us": round(us, 2)}
+            each = [1e3 * he.elapsed_ms(*raw[s][i]) for s in range(args.steps)]
+        us = float(np.mean(each))
+        # mean (used for the rates below), median and minimum over the K launches
+        info = {"us": round(us, 2), "us_median": round(float(np.median(each)), 2), "us_min": round(min(each), 2)}
         if "flops" in work:
             info["TFLOP/s"] = round(work["flops"] / us / 1e6, 1)
             info["frac_fp8_peak"] = round(work["flops"] / us / 1e6 / PEAK_FP8_TFLOPS, 4)
