@@ -307,16 +307,15 @@ class ClockSampler:
         self.error = None
         self._stop = threading.Event()
         self._thread = None
-        self._handle = None
-        try:
-            import amdsmi
 
-            amdsmi.amdsmi_init()
-            self._handle = self._match(amdsmi, amdsmi.amdsmi_get_processor_handles())
-            self._metrics = lambda: amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-            self._metrics()
-        except Exception as e:  # the benchmark runs on without the clock record
-            self._handle, self.error = None, f"{type(e).__name__}: {' '.join(str(e).split())}"
+    def _open(self):
+        """amdsmi's metrics reader for torch's device 0 (on the sampler thread, so that the benchmark never
+        waits on amdsmi)."""
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = self._match(amdsmi, amdsmi.amdsmi_get_processor_handles())
+        return lambda: amdsmi.amdsmi_get_gpu_metrics_info(handle)
 
     @staticmethod
     def _match(amdsmi, handles):
@@ -336,10 +335,15 @@ class ClockSampler:
         raise RuntimeError(f"{len(handles)} GPUs and none matched to torch's device 0")
 
     def _run(self):
+        try:
+            metrics = self._open()
+        except Exception as e:  # the benchmark runs on without the clock record
+            self.error = f"{type(e).__name__}: {' '.join(str(e).split())}"
+            return
         last = None
         while not self._stop.is_set():
             try:
-                m = self._metrics()
+                m = metrics()
             except Exception as e:
                 self.error = f"{type(e).__name__}: {' '.join(str(e).split())}"
                 return
@@ -354,14 +358,15 @@ class ClockSampler:
     def start(self):
         import threading
 
-        if self._handle is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
 
     def stop(self):
         self._stop.set()
         if self._thread is not None:
             self._thread.join(timeout=1.0)
+            if self._thread.is_alive() and self.error is None:
+                self.error = "amdsmi did not answer within 1 s of the end of the timed region"
 
     def record(self, busy_from: float, busy_to: float, window_s: float = 1.05):
         """Clocks over the refreshes whose whole averaging window (about a second before each) lies in

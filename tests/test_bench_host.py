@@ -42,3 +42,19 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_sampler_start_and_stop_do_not_block():
+    """start() and stop() return promptly whether or not amdsmi finds a driver (without one, as on a host
+    with no GPU, the record carries the reason)."""
+    import time
+
+    s = bench.ClockSampler()
+    t0 = time.perf_counter()
+    s.start()
+    time.sleep(0.05)
+    s.stop()
+    assert time.perf_counter() - t0 < 5.0
+    r = s.record(0.0, 1e18)
+    assert isinstance(r["windows"], int)
+    assert "error" not in r or (isinstance(r["error"], str) and r["error"])
