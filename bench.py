@@ -16,7 +16,10 @@ steps with an event pair around every launch.  `roofline` describes the dominant
 MI355X's published peaks; its `traffic` (HBM bytes per launch) is read from the committed rocprofv3
 summary of that kernel and workload under profiles/, and is null when the kernel sources have changed since
 the counters were taken (the summary records their SHA-256).  `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Each kernel's entry gives the mean (the rates use it), median and
+minimum of its K launch durations.  `gpu_clock` is the graphics clock of each XCD while the steps ran (the
+device's metrics table through amdsmi, about one refresh a second, hence the 2.5 s settle), and MFMA-bound
+lines add the FP8 peak at that clock.
 
 The decode workload's weight (132 MB) would fit in the 256 MB Infinity Cache, so the bench keeps four
 copies and rotates them step by step: every step streams its weight from HBM, as a model with many layers
