@@ -95,6 +95,55 @@ def test_lossless_case_matches_float64_matmul():
     say(f"  lossless: max err/bound {ratio:.3g}, max |err|/B {np.max(np.abs(c - ref) / refB):.3g}")
 
 
+def extreme_scale_operands(M, N, K, seed):
+    """Codes below 1/16 in magnitude (so a 128-deep partial sum stays under 1/2) with scales that put s_a*s_w
+    near both ends of the fp32 range: K-block 1 at up to 2^127 (just below the fp32 maximum), K-block 2 in
+    the fp32 subnormals (about 2^-142), K-block 3 mixed (2^60 * 2^-100), the rest near 1."""
+    g = np.random.default_rng(seed)
+    small = np.array([c | sgn for c in range(0x18) for sgn in (0, 0x80)], np.uint8)
+    qa = small[g.integers(0, len(small), (M, K))]
+    qw = small[g.integers(0, len(small), (N, K))]
+    sa = g.uniform(1, 2, (K // 128, M)).astype(np.float32)
+    sw = g.uniform(1, 2, (N // 128, K // 128)).astype(np.float32)
+    sa[1] *= np.float32(2.0 ** 62)
+    sw[:, 1] *= np.float32(2.0 ** 63)
+    sa[2] *= np.float32(2.0 ** -70)
+    sw[:, 2] *= np.float32(2.0 ** -72)
+    sa[3] *= np.float32(2.0 ** 60)
+    sw[:, 3] *= np.float32(2.0 ** -100)
+    return qa, sa, qw, sw
+
+
+@pytest.mark.parametrize("M", [300, 64])   # the large-M and the small-M kernel
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_scales_near_the_ends_of_the_fp32_range(M, out):
+    """The promotion forms s_a * s_w in fp32; with products up to 2^127 and down into the subnormals (and
+    outputs that stay finite) the result meets the bound like any other."""
+    N, K = 256, 512
+    qa, sa, qw, sw = extreme_scale_operands(M, N, K, 77)
+    c = fq.fp8q_gemm_blockscaled(u8_dev(qa), f32_dev(sa), u8_dev(qw), f32_dev(sw), out_dtype=DT[out])
+    C, B = oracle.gemm_blockscaled(qa, sa, qw, sw)
+    got = gemm_out_to_f64(c)
+    assert np.all(np.isfinite(got)) and np.max(np.abs(C)) > 2.0 ** 115
+    ratio = assert_gemm_within_bound(got, C, B, out == "bf16", f"extreme scales M={M}")
+    say(f"  extreme scales M={M} {out}: max |C| 2^{np.log2(np.max(np.abs(C))):.1f}, max err/bound {ratio:.3g}")
+
+
+def test_grouped_scales_near_the_ends_of_the_fp32_range():
+    """The same operands through the grouped kernel: two experts of 128 and 256 rows."""
+    N, K = 256, 512
+    qa, sa, qw0, sw0 = extreme_scale_operands(384, N, K, 78)
+    _, _, qw1, sw1 = extreme_scale_operands(8, N, K, 79)
+    qw, sw = np.stack([qw0, qw1]), np.stack([sw0, sw1])
+    off = np.array([0, 128, 384], np.int32)
+    c = fq.fp8q_grouped_gemm_blockscaled(u8_dev(qa), f32_dev(sa), u8_dev(qw), f32_dev(sw),
+                                         torch.from_numpy(off).cuda(), out_dtype=torch.float32)
+    C, B = oracle.grouped_gemm_blockscaled(qa, sa, qw, sw, off)
+    got = gemm_out_to_f64(c)
+    assert np.all(np.isfinite(got))
+    assert_gemm_within_bound(got, C, B, False, "grouped extreme scales")
+
+
 def test_deterministic():
     d = wl.tiny()
     c1 = host(gpu_path(d["a"], d["w"], "f32"))
