@@ -181,10 +181,11 @@ int fp8q_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t 
  *   qw : E4M3 [N, K],  sw : fp32 [N/128][K/128]
  *   c  : [M, N] bf16 (out_dtype FP8Q_OUT_BF16, round to nearest even) or fp32 (FP8Q_OUT_F32)
  * Requires M >= 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23.
- * Range: each promotion multiplies by s_a * s_w formed in fp32, so the result is
- * accurate while every such product is finite in fp32 (for scales from the
- * quantizers: amax_a * amax_w <= 448^2 * FLT_MAX, about 6.8e43); past that the
- * output may be +-inf or NaN.  The same holds for the grouped GEMMs below. */
+ * Range: each promotion multiplies by s_a * s_w formed in fp32 and adds into an
+ * fp32 sum, so the result is accurate while every such product and every running
+ * sum is finite in fp32 (for scales from the quantizers the products are finite
+ * when amax_a * amax_w <= 448^2 * FLT_MAX, about 6.8e43); past that the output may
+ * be +-inf or NaN.  The same holds for the grouped GEMMs below. */
 int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                           int out_dtype, int64_t M, int64_t N, int64_t K, void *stream);
 
