@@ -68,6 +68,12 @@ MUTATIONS = {
     "e5m6_divisor_fp16_max": ("float scale = amax / 65024.0f;", "float scale = amax / 65504.0f;"),
     "e5m6_pair_order_swapped": ("out[j / 2 * 3 + 1] = (uint8_t)((c[0] >> 8) | ((c[1] & 0xFu) << 4));",
                                 "out[j / 2 * 3 + 1] = (uint8_t)((c[1] >> 8) | ((c[0] & 0xFu) << 4));"),
+    "act_amax_skips_last_element": ("for (int j = 0; j < GROUP; j++) {\n                float v = bf16_to_f32(g[j]);\n                if (!isfinite(v)) bad = 1;\n                float av = fabsf(v);",
+                                    "for (int j = 0; j < GROUP - 1; j++) {\n                float v = bf16_to_f32(g[j]);\n                if (!isfinite(v)) bad = 1;\n                float av = fabsf(v);"),
+    "fp4_weight_amax_one_row": ("const uint16_t *row = w + (nb * GROUP + i) * K + kb * GROUP;\n                for (int j = 0; j < GROUP; j++) {\n                    float v = bf16_to_f32(row[j]);\n                    if (!isfinite(v)) bad = 1;\n                    if (fabsf(v) > amax) amax = fabsf(v);\n                }\n            }\n            float scale = amax / 6.0f;",
+                                "const uint16_t *row = w + (nb * GROUP) * K + kb * GROUP;\n                for (int j = 0; j < GROUP; j++) {\n                    float v = bf16_to_f32(row[j]);\n                    if (!isfinite(v)) bad = 1;\n                    if (fabsf(v) > amax) amax = fabsf(v);\n                }\n            }\n            float scale = amax / 6.0f;"),
+    "e5m6_no_saturation": ("    if (a >= e5m6_magnitude(E5M6_MAX_CODE)) return (uint16_t)(sign | E5M6_MAX_CODE);\n", ""),
+    "e5m6_third_byte_shift": ("out[j / 2 * 3 + 2] = (uint8_t)(c[1] >> 4);", "out[j / 2 * 3 + 2] = (uint8_t)(c[1] >> 8);"),
     "swiglu_sigmoid_sign": ("double v = p / (1.0 + exp(-xv));", "double v = p / (1.0 + exp(xv));"),
     "swiglu_fp32_intermediate": ("double v = p / (1.0 + exp(-xv));", "double v = (double)(float)(p / (1.0 + exp(-xv)));"),
     "swiglu_tiny_gate_side_flipped": ("xv > 0 ? 1 : -1", "xv > 0 ? -1 : 1"),
