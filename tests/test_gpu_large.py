@@ -2,7 +2,8 @@
 pass 2^32 (and its 32-bit buffer offsets must stay relative to a tile or row base).  Inputs are drawn on
 the device from seeded torch generators (random bf16 values, or random finite E4M3 codes and scales); the
 oracle sees host copies of the sampled rows, blocks or columns, which include the rows on both sides of
-each 2^32-byte boundary."""
+each 2^32-byte boundary.  The GEMMs also run at the largest K they accept (2^23), where a tile's 32-bit
+offsets come closest to their limit."""
 import numpy as np
 import pytest
 import torch
@@ -200,3 +201,36 @@ def test_e5m6_quant_past_4gib():
     oq, os_ = oracle.quant_act_e5m6_1x128(host(x[ri]))
     assert np.array_equal(host(q[ri]), oq)
     assert np.array_equal(host(s[:, ri]).view(np.uint32), os_.view(np.uint32))
+
+
+KMAX = 2 ** 23                  # the largest K the GEMMs accept: a 256-row tile then spans 2^31 bytes
+
+
+def codes_k(rows, k, seed):
+    """Random finite E4M3 codes [rows, k] (the NaN codes left out)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    r = torch.randint(0, 254, (rows, k), device="cuda", generator=g, dtype=torch.int16)
+    return (r + (r >= 127).to(torch.int16)).to(torch.uint8)
+
+
+@pytest.mark.parametrize("M", [300, 64])   # the large-M kernel (a whole and a partial M tile) and small-M
+def test_gemm_at_the_largest_k(M):
+    """K = 2^23 (65,536 K-blocks): the last row of a 256-row tile starts 255 * 2^23 bytes into it, so the
+    per-lane buffer offsets reach 2^31 - 16.  Sampled rows (both ends of each M tile) x sampled columns of
+    both 128-row weight blocks.  (Summing 65,536 promoted partials in fp32 has a worst-case rounding error
+    of about 4e-3 B, above the bound; random signs keep the actual error far below it.)"""
+    N = 256
+    qa, sa = codes_k(M, KMAX, 120), scales((KMAX // 128, M), 121)
+    qw, sw = codes_k(N, KMAX, 122), scales((N // 128, KMAX // 128), 123)
+    say(f"large: gemm A [{M}, 2^23] x W [{N}, 2^23]")
+    c = fq.fp8q_gemm_blockscaled(qa, sa, qw, sw, out_dtype=torch.float32)
+    rows = np.array(sorted({0, 1, min(255, M - 1), M - 1} | ({256, 257} if M > 256 else set())))
+    cols = np.array([0, 5, 127, 128, 200, 255])
+    ri = torch.from_numpy(rows).cuda()
+    ha, hs = host(qa[ri]), host(sa[:, ri])
+    del qa, sa
+    C, B = oracle.gemm_blockscaled(ha, hs, host(qw), host(sw), cols=cols)
+    got = gemm_out_to_f64(c[ri][:, torch.from_numpy(cols).cuda()])
+    ratio = assert_gemm_within_bound(got, C, B, False, f"K = 2^23, M = {M}")
+    say(f"  max err/bound {ratio:.3g}")
