@@ -230,6 +230,29 @@ def test_grouped_skewed_with_empty_expert(out):
         assert np.all(c[off[e] + cnt:off[e + 1]] == 0.0)
 
 
+@pytest.mark.parametrize("E", [130, 256])
+def test_grouped_more_than_64_experts(E):
+    """A tile's expert is found by a prefix sum over the offsets, 64 experts per pass: with 130 and 256
+    experts (DeepSeek-V3 routes over 256) the tiles of experts in every pass, the empty experts between them
+    and a partial last pass must all land on the right weights."""
+    g = np.random.default_rng(E)
+    counts = g.integers(0, 300, size=E)
+    counts[g.random(E) < 0.4] = 0                           # many empty experts
+    counts[[0, 63, 64, 127, 128, E - 1]] = [5, 260, 128, 1, 257, 40]
+    ab, wb, off = grouped_case(31, counts.tolist(), 128, 256)
+    say(f"grouped gemm: E={E} experts, {int(off[-1])} rows")
+    qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(ab))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(wb))
+    c = gemm_out_to_f64(fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda(),
+                                                         out_dtype=torch.float32))
+    oqa, osa = oracle.quant_act_1x128(ab)
+    oqw, osw = oracle.quant_w_128x128(wb)
+    C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, off)
+    assert_gemm_within_bound(c, C, B, False, f"grouped, {E} experts")
+    for e, cnt in enumerate(counts):                       # padding rows are exactly zero
+        assert np.all(c[off[e] + cnt:off[e + 1]] == 0.0)
+
+
 def test_grouped_offsets_outside_the_rules():
     """Offsets that break the layout rules (the header's promise for them): segments that end before
     M_total leave the rows after them untouched, and a last offset past M_total is cut at M_total."""

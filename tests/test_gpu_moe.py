@@ -171,7 +171,8 @@ def same_bits(a, b):
 
 
 @pytest.mark.parametrize("T,K,N,E,k,out", [(300, 512, 256, 64, 8, torch.bfloat16), (5, 128, 384, 4, 2, torch.float32),
-                                           (0, 256, 128, 8, 2, torch.bfloat16), (1000, 1024, 512, 16, 4, torch.float32)])
+                                           (0, 256, 128, 8, 2, torch.bfloat16), (1000, 1024, 512, 16, 4, torch.float32),
+                                           (1000, 256, 128, 256, 8, torch.bfloat16)])   # 256 experts
 def test_gather_fused_grouped_gemm_matches_gather_then_gemm(T, K, N, E, k, out):
     """Bit-identical to gathering the rows first, padding rows exactly 0, rows past the layout untouched, and
     within the GEMM bound of the oracle on every row."""
