@@ -68,6 +68,22 @@ def test_shapes_all_elements(M, N, K, out):
     assert_gemm_within_bound(c, C, B, out == "bf16", f"{M}x{N}x{K}")
 
 
+# N -> the small-M kernel's slice (8 * ceil(N / 2048) rows, at most 80) and so its subtile count NSUB:
+# 4352 -> 24 rows (NSUB 2), 6144 -> 24 (2), 8320 -> 40 (3), 10240 -> 40 (3), 12416 -> 56 (4), 16384 -> 64 (4)
+@pytest.mark.parametrize("M,N,out", [(64, 4352, "bf16"), (17, 6144, "f32"), (64, 8320, "f32"), (40, 10240, "bf16"),
+                                     (64, 12416, "bf16"), (1, 16384, "f32")])
+def test_small_m_slice_widths(M, N, out):
+    """Every subtile count of the small-M kernel, including slices that end in half a subtile."""
+    K = 384
+    g = np.random.default_rng([61, M, N])
+    ab = wl.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    wb = wl.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say(f"gemm small-M: M={M} N={N} K={K} {out}")
+    c = gemm_out_to_f64(gpu_path(ab, wb, out))
+    C, B = oracle_path(ab, wb)
+    assert_gemm_within_bound(c, C, B, out == "bf16", f"small-M {M}x{N}")
+
+
 def test_lossless_case_matches_float64_matmul():
     """Inputs that quantize exactly (e4m3 values times one power of two per group, each group holding
     +-448 * 2^k): the GPU result must match numpy's float64 product of the bf16 inputs within the bound."""
