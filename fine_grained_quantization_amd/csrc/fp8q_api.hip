@@ -201,7 +201,8 @@ int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint
     if (!qa || !sa || !qw || !sw || !c || !off) return FP8Q_ERR_NULL;
     if (!aligned16(qa) || !aligned16(sa) || !aligned16(qw) || !aligned16(sw) || !aligned16(c)) return FP8Q_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(off) & 3u) != 0) return FP8Q_ERR_ALIGN;
-    if (fp8q::gemm_blocks(M_total, N) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    const int64_t blocks = fp8q::grouped_gemm_blocks(M_total, N, E);
+    if (blocks < 0 || blocks > kMaxGrid) return FP8Q_ERR_SHAPE;
     int rc = check_device();
     if (rc) return rc;
     return finish(fp8q::launch_grouped_gemm_blockscaled(qa, sa, qw, sw, c, out_dtype == FP8Q_OUT_BF16, off, E,
@@ -222,7 +223,8 @@ int fp8q_grouped_gemm_blockscaled_gather(const uint8_t *q, const float *s, int64
     if (!aligned16(qw) || !aligned16(sw) || !aligned16(c) || !aligned4(off) || !aligned4(row_token) ||
         (T > 0 && (!aligned16(q) || !aligned4(s))))
         return FP8Q_ERR_ALIGN;
-    if (fp8q::gemm_blocks(M_total, N) > kMaxGrid) return FP8Q_ERR_SHAPE;
+    const int64_t blocks = fp8q::grouped_gemm_blocks(M_total, N, E);
+    if (blocks < 0 || blocks > kMaxGrid) return FP8Q_ERR_SHAPE;
     int rc = check_device();
     if (rc) return rc;
     return finish(fp8q::launch_grouped_gemm_gather(q, s, T, row_token, qw, sw, c, out_dtype == FP8Q_OUT_BF16, off, E,

@@ -245,6 +245,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint64_t bytes) {
     return r;
 }
 
+// The same resource with a byte count of 0: every load through it is out of range and returns zeros without
+// touching memory, whatever its per-lane and scalar offsets.
+__device__ __forceinline__ i32x4 empty_rsrc(i32x4 r) {
+    r[2] = 0;
+    return r;
+}
+
 // Per-lane source offsets of one K-block tile.  Rows are copied 8 at a time (1 KB per instruction); lane l of
 // an instruction lands in LDS slot l, i.e. row l / 8 of the 8, physical chunk l % 8, which must hold logical
 // chunk (l % 8) ^ swzf(row).  Wave w copies A rows [32 w, 32 w + 32) and the W row groups g = w, w + 8, ...
@@ -319,21 +326,26 @@ struct TileLoader {
             wvoff[j] = (int)(r * K) + (((lane & 7) ^ swzf(r)) << 4);
         }
     }
-    // Copies K-block kb (or, for koff == kOutOfRange, nothing) into `stage`; the scales of K-block ks
-    // (kb, clamped to the last block) come along, one dword per lane from in-bounds addresses.
-    __device__ __forceinline__ void issue(uint8_t *stage, int koff, int64_t ks, int wave) const {
+    // Copies K-block kb (koff = kb * 128) into `stage`, or, when `tiles` is false, no tile bytes at all: the
+    // tile resources are then given zero bytes, so that every lane's load is out of range (and reads zeros)
+    // whatever its offsets.  The scales of K-block ks (kb, clamped to the last block) come along, one dword
+    // per lane from in-bounds addresses.
+    __device__ __forceinline__ void issue(uint8_t *stage, bool tiles, int koff, int64_t ks, int wave) const {
         const bool act = wave < 4;  // wave-uniform: the resource and offset are scalar selects
         const i32x4 rs = act ? make_rsrc(sa_tile + ks * M, sa_bytes) : rsw;
         fp8q_raw_buffer_load_lds(rs, (lds_ptr)(stage + kScOff + wave * 256), 4, scvoff, act ? 0 : (int)(ks * 4), 0,
                                  0);
+        const i32x4 ta = tiles ? ra : empty_rsrc(ra);  // `tiles` is wave-uniform: scalar selects
+        const i32x4 tw = tiles ? rw : empty_rsrc(rw);
+        const int so = tiles ? koff : 0;
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            fp8q_raw_buffer_load_lds(ra, (lds_ptr)(stage + (wave * 32 + j * 8) * 128), 16, avoff[j], koff, 0, 0);
+            fp8q_raw_buffer_load_lds(ta, (lds_ptr)(stage + (wave * 32 + j * 8) * 128), 16, avoff[j], so, 0, 0);
 #pragma unroll
         for (int j = 0; j < kWPerWave; j++) {
             const int g = wave + 8 * j;
             if (g < kWGroups)  // wave-uniform
-                fp8q_raw_buffer_load_lds(rw, (lds_ptr)(stage + kBig * 128 + g * 1024), 16, wvoff[j], koff, 0, 0);
+                fp8q_raw_buffer_load_lds(tw, (lds_ptr)(stage + kBig * 128 + g * 1024), 16, wvoff[j], so, 0, 0);
         }
     }
 };
@@ -395,14 +407,18 @@ __device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restric
     n0 = (T % n_ntiles) * bn;
     // The expert owning M tile mt: a prefix sum of the experts' tile counts, 64 experts per pass (lane i
     // holds expert base + i), and the first lane whose running total exceeds mt.
+    // A segment is cut to [0, M) before its tiles are counted (in 64-bit arithmetic), so offsets that break
+    // the layout rules can neither overflow the count nor yield rows outside the buffer.
     int64_t before = 0;
     for (int64_t base = 0; base < E; base += 64) {
         const int64_t i = base + lane;
         int lo = 0, hi = 0, cnt = 0;
         if (i < E) {
-            lo = off[i];
-            hi = off[i + 1];
-            cnt = hi > lo ? (hi - lo + kBig - 1) / kBig : 0;
+            const int64_t l = (int64_t)off[i] < 0 ? 0 : ((int64_t)off[i] > M ? M : (int64_t)off[i]);
+            const int64_t h = (int64_t)off[i + 1] < l ? l : ((int64_t)off[i + 1] > M ? M : (int64_t)off[i + 1]);
+            lo = (int)l;
+            hi = (int)h;
+            cnt = (int)((h - l + kBig - 1) / kBig);
         }
         int incl = cnt;
 #pragma unroll
@@ -417,10 +433,8 @@ __device__ __forceinline__ bool grouped_tile(int64_t t, const int32_t *__restric
             const int lo_e = __shfl(lo, L, 64), hi_e = __shfl(hi, L, 64);
             const int64_t first = before + __shfl(incl, L, 64) - __shfl(cnt, L, 64);
             m0 = lo_e + (mt - first) * kBig;
-            mend = hi_e < M ? hi_e : M;
-            // offsets that break the layout rules (decreasing, negative, past M) yield no rows, never a
-            // range outside [0, M)
-            return m0 >= 0 && m0 < mend;
+            mend = hi_e;
+            return m0 < mend;
         }
         before += __shfl(incl, 63, 64);
     }
@@ -473,7 +487,7 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
 #pragma unroll
         for (int mi = 0; mi < 4; mi++) acc[ni][mi] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    ld.issue(stage0, 0, 0, wave);
+    ld.issue(stage0, true, 0, 0, wave);
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
     for (int64_t kb = 0; kb < KB; kb++) {
@@ -484,7 +498,7 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
         __syncthreads();
         // The prefetch is unconditional (past the last K-block it copies no tiles and yields zeros), so
         // the loop body is a single basic block.
-        ld.issue(nxt, kb + 1 < KB ? (int)((kb + 1) * 128) : kOutOfRange, kb + 1 < KB ? kb + 1 : kb, wave);
+        ld.issue(nxt, kb + 1 < KB, (int)((kb + 1) * 128), kb + 1 < KB ? kb + 1 : kb, wave);
         // The first weight fragment is read before the activation fragments so that the first MFMA waits
         // for two LDS reads, not five.  The fragment of weight subtile ni+1 is read while the 4 MFMAs of
         // subtile ni run; their partials are promoted right after issue (the first MFMA has finished by
@@ -728,17 +742,21 @@ hipError_t launch_256(const uint8_t *qa, const float *sa, const uint8_t *qw, con
     }
 }
 
+// Tile rows of a grouped launch over M rows and E experts: enough for any offsets that do not decrease.
+int64_t grouped_mtiles(int64_t M, int64_t E) { return M / kBig + E; }
+
 template <bool OUT_BF16>
 hipError_t launch_256_grouped(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                               int64_t M, int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
     constexpr int64_t BN = 256;
     const int64_t n_ntiles = (N + BN - 1) / BN;
-    // Every expert owns ceil(len / 256) tiles; since lengths are multiples of 128 that is at most
-    // len / 256 + 1/2 each, so M / 256 + ceil(E / 2) tile rows cover all experts.
-    const int64_t n_mtiles = M / kBig + (E + 1) / 2;
+    // Every expert owns ceil(len / 256) tiles of its segment cut to [0, M).  When the offsets do not decrease
+    // the cut segments are disjoint, so the counts add up to at most M / 256 + E tile rows (M / 256 + E / 2
+    // when every length is a multiple of 128); the rows past the real tiles exit at once.
+    const int64_t n_mtiles = grouped_mtiles(M, E);
     // whole rounds of 256 workgroups: the XCD permutation of the tile index is a bijection on each round,
     // and the indices past the last tile exit at once
-    const int64_t blocks = (n_mtiles * n_ntiles + 255) / 256 * 256;
+    const int64_t blocks = grouped_gemm_blocks(M, N, E);
     gemm_bs_256_kernel<OUT_BF16, true, 8, 0><<<dim3((unsigned)blocks), 512, 0, stream>>>(
         qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0);
     return hipGetLastError();
@@ -751,8 +769,8 @@ hipError_t launch_256_grouped_gather(const uint8_t *q, const float *s, int64_t T
                                      const int32_t *off, int64_t E, hipStream_t stream) {
     constexpr int64_t BN = 256;
     const int64_t n_ntiles = (N + BN - 1) / BN;
-    const int64_t n_mtiles = M / kBig + (E + 1) / 2;
-    const int64_t blocks = (n_mtiles * n_ntiles + 255) / 256 * 256;
+    const int64_t n_mtiles = grouped_mtiles(M, E);
+    const int64_t blocks = grouped_gemm_blocks(M, N, E);
     gemm_bs_256_kernel<OUT_BF16, true, 8, 0, true><<<dim3((unsigned)blocks), 512, 0, stream>>>(
         q, s, qw, sw, c, M, N, K, off, E, n_mtiles, n_ntiles, blocks, N, 0, rtok, T);
     return hipGetLastError();
@@ -839,20 +857,25 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
     // Per K-block: wait for its copies, read all its fragments into registers, then start the copies of the
     // wave's next K-block into the (now free) slot, and only then run the MFMAs and promotions, which
     // overlap with those copies.
+    // Past the last K-block (kb >= KB, wave-uniform) the resources are given zero bytes, so every load reads
+    // zeros without touching memory.
     auto issue = [&](int kb) {
-        const int so = kb < KB ? kb * 128 : kOutOfRange;
+        const bool in = kb < KB;
+        const int so = in ? kb * 128 : 0;
+        const i32x4 tw = in ? rw : empty_rsrc(rw), ta = in ? rA : empty_rsrc(rA);
+        const i32x4 ts = in ? rS : empty_rsrc(rS), tsw = in ? rSW : empty_rsrc(rSW);
 #pragma unroll
         for (int j = 0; j < 2 * NSUB; j++)
-            fp8q_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(wslot + j * 1024), 16, w_voff[j],
+            fp8q_raw_buffer_load_lds(tw, (__attribute__((address_space(3))) void *)(wslot + j * 1024), 16, w_voff[j],
                                      so, 0, 0);
 #pragma unroll
         for (int j = 0; j < 8; j++)
-            fp8q_raw_buffer_load_lds(rA, (__attribute__((address_space(3))) void *)(aslot + j * 1024), 16, a_voff[j],
+            fp8q_raw_buffer_load_lds(ta, (__attribute__((address_space(3))) void *)(aslot + j * 1024), 16, a_voff[j],
                                      so, 0, 0);
-        fp8q_raw_buffer_load_lds(rS, (__attribute__((address_space(3))) void *)(aslot + kA), 4, lane * 4,
-                                 kb < KB ? kb * (int)M * 4 : kOutOfRange, 0, 0);
-        fp8q_raw_buffer_load_lds(rSW, (__attribute__((address_space(3))) void *)(aslot + kA + 256), 4, sw_voff,
-                                 kb < KB ? kb * 4 : kOutOfRange, 0, 0);
+        fp8q_raw_buffer_load_lds(ts, (__attribute__((address_space(3))) void *)(aslot + kA), 4, lane * 4,
+                                 in ? kb * (int)M * 4 : 0, 0, 0);
+        fp8q_raw_buffer_load_lds(tsw, (__attribute__((address_space(3))) void *)(aslot + kA + 256), 4, sw_voff,
+                                 in ? kb * 4 : 0, 0, 0);
     };
 
     const int NI = (KB + kDecWaves - 1) / kDecWaves;
@@ -972,6 +995,13 @@ hipError_t launch(const uint8_t *qa, const float *sa, const uint8_t *qw, const f
 }
 
 }  // namespace
+
+int64_t grouped_gemm_blocks(int64_t M, int64_t N, int64_t E) {
+    if (M < 0 || N < 0 || E < 1 || E > (int64_t(1) << 31)) return -1;
+    const int64_t mt = grouped_mtiles(M, E), nt = (N + 255) / 256;
+    if (nt > 0 && mt > (int64_t(1) << 40) / nt) return -1;
+    return (mt * nt + 255) / 256 * 256;
+}
 
 int64_t gemm_blocks(int64_t M, int64_t N) {
     return ((M + kBM - 1) / kBM) * (N / kBN) + 8 * 1024;  // generous upper bound over both kernels

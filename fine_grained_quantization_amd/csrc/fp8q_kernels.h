@@ -46,5 +46,8 @@ hipError_t launch_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, in
                                  int64_t rows, uint8_t *qa, float *sa, hipStream_t stream);
 // Number of workgroups the dense GEMM launches for an M x N output (for grid-size validation).
 int64_t gemm_blocks(int64_t M, int64_t N);
+// Number of workgroups a grouped GEMM launches for M rows, N columns and E experts; -1 when that count
+// would pass 2^40 or E is past 2^31 (for grid-size validation).
+int64_t grouped_gemm_blocks(int64_t M, int64_t N, int64_t E);
 
 }  // namespace fp8q

@@ -189,8 +189,15 @@ int fp8q_dequant_w_128x128(const uint8_t *q, const float *s, int64_t N, int64_t 
 int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                           int out_dtype, int64_t M, int64_t N, int64_t K, void *stream);
 
-/* Grouped block-scaled FP8 GEMM for MoE experts (one Linear per expert; the
- * token-to-expert layout is the caller's):
+/* Grouped block-scaled FP8 GEMM for MoE experts.  Each routed expert applies
+ * its own Linear to the tokens sent to it (page "The Definitive Information To
+ * Deepseek", the passages on the MoE models' all-to-all communication, where
+ * each token goes to a few experts spread over nodes); the tokens are mapped to
+ * experts and laid out expert by expert beforehand (page "DeepSeek starts
+ * updating frequently", the TileKernels feature list: MoE routing maps tokens
+ * to experts), so each expert's Linear is one contiguous segment of rows.  The
+ * GEMM of every segment is the block-scaled FP8 GEMM above with that expert's
+ * weight and block scales; the token-to-expert layout is the caller's:
  *   rows [off[e], off[e+1]) of A are multiplied by expert e's weight.
  *   qa  : E4M3 [M_total, K],      sa : fp32 [K/128][M_total]
  *   qw  : E4M3 [E][N][K],         sw : fp32 [E][N/128][K/128]
@@ -202,10 +209,14 @@ int fp8q_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw,
  *         (fp8q_moe_route_capacity) without reading off[E] back to the host.
  *   c   : [M_total, N] bf16 or fp32.
  * Requires E >= 1, M_total % 128 == 0, N % 128 == 0, K % 128 == 0, 128 <= K <= 2^23.
- * The offsets live on the device and are not checked on the host.  When they
- * break the rules above, rows that no segment covers are left unwritten (c keeps
- * its previous contents there), and every memory access still stays inside the
- * buffers described by M_total, E, N and K. */
+ * The offsets live on the device and are not checked on the host.  Offsets that
+ * never decrease but break the other rules (segments that are not multiples of
+ * 128 rows, off[0] > 0, offsets past M_total) are cut to [0, M_total): every row
+ * a cut segment covers is computed with that segment's expert, and the rows no
+ * segment covers are left unwritten (c keeps its previous contents there).  When
+ * the offsets decrease somewhere, segments may overlap and the output rows are
+ * unspecified.  In every case each memory access stays inside the buffers
+ * described by M_total, E, N and K. */
 int fp8q_grouped_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
                                   int out_dtype, const int32_t *off, int64_t E, int64_t M_total, int64_t N,
                                   int64_t K, void *stream);

@@ -205,9 +205,19 @@ def sample_rows(M, n, seed):
     return np.array(sorted(rows))
 
 
+# Whole 256-row x 256-column output blocks checked element by element at full K: (first row, first column).
+# Up (N = 18432) runs 256 x 256 tiles over columns [0, 16384) and 256 x 128 tiles over the rest; down
+# (N = 7168) 256 x 256 tiles over [0, 4096) and 256 x 192 tiles over the rest, so the blocks below cover a
+# main tile, a block straddling the last main and first tail column, and the last tail tiles.
+WHOLE_TILES = {"up": [(1792, 8192), (3840, 16256), (0, 18176)],
+               "down": [(2048, 1024), (1792, 3968), (3840, 6912)]}
+
+
 @pytest.mark.parametrize("name,out", [("up", "bf16"), ("up", "f32"), ("down", "bf16"), ("down", "f32")])
 def test_full_size_dense_sampled(name, out):
-    """Full-size FFN projections; every output column of sampled rows and every row of sampled columns."""
+    """Full-size FFN projections: every output column of sampled rows, every row of sampled columns, and whole
+    256 x 256 output blocks (every element of a tile at full K).  bf16 outputs also report the literal
+    bound's ratio (without the allowance for their own final rounding)."""
     d = wl.dense_up() if name == "up" else wl.dense_down()
     if name == "down":   # A = bf16(SiLU(x) * y), from the oracle
         d["a"] = oracle.swiglu_bf16(d["x"], d["y"])
@@ -219,9 +229,18 @@ def test_full_size_dense_sampled(name, out):
     qw, sw = oracle.quant_w_128x128(d["w"])
     C, B = oracle.gemm_blockscaled(qa, sa, qw, sw, rows=rows)
     r1 = assert_gemm_within_bound(c[rows], C, B, out == "bf16", f"{name} rows")
+    lit = [literal_bound_ratio(c[rows], C, B)]
     C, B = oracle.gemm_blockscaled(qa, sa, qw, sw, cols=cols)
     r2 = assert_gemm_within_bound(c[:, cols], C, B, out == "bf16", f"{name} cols")
-    say(f"  max err/bound rows {r1:.3g} cols {r2:.3g}")
+    lit.append(literal_bound_ratio(c[:, cols], C, B))
+    r3 = 0.0
+    for m0, n0 in WHOLE_TILES[name]:
+        tr, tc = np.arange(m0, m0 + 256), np.arange(n0, n0 + 256)
+        C, B = oracle.gemm_blockscaled(qa, sa, qw, sw, rows=tr, cols=tc)
+        got = c[m0:m0 + 256, n0:n0 + 256]
+        r3 = max(r3, assert_gemm_within_bound(got, C, B, out == "bf16", f"{name} block ({m0}, {n0})"))
+        lit.append(literal_bound_ratio(got, C, B))
+    say(f"  max err/bound rows {r1:.3g} cols {r2:.3g} whole blocks {r3:.3g}; literal-bound ratio {max(lit):.3g}")
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -233,7 +252,8 @@ def test_decode_small_m_full_size(out):
     c = gemm_out_to_f64(fq.fp8q_gemm_blockscaled(qa, sa, u8_dev(d["wq"]), f32_dev(d["sw"]), out_dtype=DT[out]))
     oqa, osa = oracle.quant_act_1x128(d["a"])
     C, B = oracle.gemm_blockscaled(oqa, osa, d["wq"], d["sw"])
-    assert_gemm_within_bound(c, C, B, out == "bf16", "decode")
+    r = assert_gemm_within_bound(c, C, B, out == "bf16", "decode")
+    say(f"  max err/bound {r:.3g}; literal-bound ratio {literal_bound_ratio(c, C, B):.3g}")
 
 
 # ------------------------------------------------------------------ grouped (MoE)
@@ -318,6 +338,35 @@ def test_grouped_offsets_outside_the_rules():
     c = fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).cuda(), out_dtype=torch.float32)
     C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, np.array([0, 256, M], np.int32))
     assert_gemm_within_bound(gemm_out_to_f64(c), C, B, False, "offset past M_total")
+
+
+@pytest.mark.parametrize("offs", [[0, 1, 2, 3, 300, 301, 384, 512], list(range(0, 129, 2))],
+                         ids=["7_experts_ragged", "64_experts_of_2_rows"])
+def test_grouped_segments_of_any_length(offs):
+    """Offsets that never decrease but are not multiples of 128 rows: each segment's rows are cut into its own
+    tiles (one or two rows can be a whole tile), so there can be more tiles than M_total / 256 + E / 2; every
+    row must still be computed with its own expert (the oracle takes any non-decreasing offsets), by the
+    grouped GEMM and by its gather form (identity row map, bit-identical)."""
+    off = np.array(offs, np.int32)
+    E, M = len(off) - 1, int(off[-1])
+    K, N = 256, 256
+    g = np.random.default_rng(len(offs))
+    ab = wl.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    wb = wl.bf16_bits((g.standard_normal((E, N, K)) * 0.02).astype(np.float32))
+    say(f"grouped gemm: {E} segments of {np.diff(off).min()}..{np.diff(off).max()} rows, M_total={M}")
+    qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(ab))
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(wb))
+    od = torch.from_numpy(off).cuda()
+    c1 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled(qa, sa, qw, sw, od, out_dtype=torch.float32, c=c1)
+    c2 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled_gather(qa, sa, torch.arange(M, dtype=torch.int32, device="cuda"), qw, sw, od,
+                                            out_dtype=torch.float32, c=c2)
+    oqa, osa = oracle.quant_act_1x128(ab)
+    oqw, osw = oracle.quant_w_128x128(wb)
+    C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, off)
+    assert_gemm_within_bound(gemm_out_to_f64(c1), C, B, False, "segments of any length")
+    assert np.array_equal(host(c1).view(np.uint32), host(c2).view(np.uint32))
 
 
 def test_grouped_gather_with_offsets_outside_the_rules():

@@ -8,8 +8,8 @@ import torch
 import fine_grained_quantization_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import (assert_gemm_within_bound, bf16_bits_to_f64, bf16_dev, f32_dev, gemm_out_to_f64, host, say,
-                      u8_dev)
+from gpu_util import (assert_gemm_within_bound, bf16_bits_to_f64, bf16_dev, f32_dev, gemm_out_to_f64, host,
+                      literal_bound_ratio, say, u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -226,3 +226,61 @@ def test_gather_fused_moe_layer(out):
     c1, c2, r = fused_and_separate(q, s, d["logits"], k, qw, sw, out)
     assert same_bits(c1, c2)
     say(f"  bit-identical over {r.M} rows")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_moe_layer_timed_path_against_oracle(out):
+    """The MoE layer exactly as the benchmark's step runs it: the tokens quantized (1x128) and routed on the
+    GPU, the expert weights quantized (128x128) on the GPU, and the grouped GEMM reading the routed token rows
+    in place, over the routing capacity.  Against the oracle's quantizers, routing, gather and grouped GEMM:
+    four rows of every expert segment (its first and last routed rows and two others) on all 2048 columns,
+    and two experts' whole segments (every row, the segment's 128-row half tile included) on two 256-column
+    blocks.  fp32 output is held to the literal bound 1e-3 B + 1e-6; bf16 output to that plus its own final
+    rounding, with the literal ratio printed.  Empty rows are exactly 0, rows past the layout untouched."""
+    d = wl.moe()
+    T, E, k, N, K = d["T"], d["E"], d["topk"], d["N"], d["K"]
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    cap = fq.fp8q_moe_route_capacity(T, E, k)
+    say(f"moe layer, timed path: T={T} E={E} k={k} N={N} K={K} out={out}, capacity {cap} rows")
+    qt, st = fq.fp8q_quant_act_1x128(bf16_dev(d["tokens"]))
+    _, off, _, row_token = fq.fp8q_moe_route_topk(f32_dev(d["logits"]), k)
+    qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(d["w"]))
+    c = torch.full((cap, N), float("nan"), dtype=dt, device="cuda")
+    fq.fp8q_grouped_gemm_blockscaled_gather(qt, st, row_token, qw, sw, off, out_dtype=dt, c=c)
+    ch = gemm_out_to_f64(c)
+
+    oqt, ost = oracle.quant_act_1x128(d["tokens"])
+    r = oracle.moe_route_topk(d["logits"], k, rows=cap)
+    assert np.array_equal(host(off), r.offsets) and np.array_equal(host(row_token), r.row_token)
+    used = r.M
+    oqa, osa = oracle.moe_gather_fp8(oqt, ost, r.row_token[:used])
+    oqw, osw = oracle.quant_w_128x128(d["w"])
+    g = np.random.default_rng(8)
+    rows = []
+    for e in range(E):
+        lo, cnt = int(r.offsets[e]), int(r.counts[e])
+        if cnt:
+            rows += [lo, lo + cnt - 1] + [lo + int(i) for i in g.integers(cnt, size=2)]
+    rows = np.array(sorted(set(rows)))
+    bf = out == "bf16"
+    C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, r.offsets, rows=rows)
+    r1 = assert_gemm_within_bound(ch[rows], C, B, bf, "moe sampled rows")
+    lit = [literal_bound_ratio(ch[rows], C, B)]
+    # whole segments: an expert whose padded length is an odd number of 128-row blocks (its last tile is the
+    # 128 x 256 layout) and one with an even number, if there is one
+    seg = np.diff(r.offsets) // 128
+    odd = [e for e in range(E) if seg[e] % 2 == 1]
+    even = [e for e in range(E) if seg[e] % 2 == 0 and seg[e] > 0]
+    r2 = 0.0
+    for e, n0 in [(odd[0] if odd else 0, 1792), (even[0] if even else E - 1, 512)]:
+        tr = np.arange(r.offsets[e], r.offsets[e + 1])
+        tc = np.arange(n0, n0 + 256)
+        C, B = oracle.grouped_gemm_blockscaled(oqa, osa, oqw, osw, r.offsets, rows=tr, cols=tc)
+        got = ch[r.offsets[e]:r.offsets[e + 1], n0:n0 + 256]
+        r2 = max(r2, assert_gemm_within_bound(got, C, B, bf, f"moe expert {e} segment, columns {n0}.."))
+        lit.append(literal_bound_ratio(got, C, B))
+    empty = np.nonzero(r.row_token[:used] < 0)[0]
+    assert np.all(ch[empty] == 0.0)
+    assert np.all(np.isnan(ch[used:]))
+    say(f"  {len(rows)} sampled rows max err/bound {r1:.3g}; whole segments {r2:.3g}; "
+        f"literal-bound ratio {max(lit):.3g}")
