@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the fine-grained FP8 Linear hot path on one MI355X.
 
-One step = the whole path over one batch of synthetic input already resident in HBM:
-  1x128 activation quantization  ->  128x128 weight quantization  ->  block-scaled FP8 GEMM (bf16 out).
-(The decode workload starts from pre-quantized weights, so its step has no weight quantization; the MoE
-workload runs the grouped GEMM over expert segments.)
+One step = the whole path over one batch of synthetic input already resident in HBM.  The default workload
+is the largest one that fits one GPU, the MoE layer: 8192 tokens x 7168 quantized 1x128, routed top-8 of 64
+experts into 128-padded expert segments, the 64 expert weights [2048, 7168] quantized 128x128, and the
+grouped block-scaled FP8 GEMM reading the routed token rows in place (bf16 out).  The dense workloads run
+1x128 activation quantization -> 128x128 weight quantization -> block-scaled FP8 GEMM; decode starts from
+pre-quantized weights, so its step has no weight quantization.  With the MoE headline, the dense up and down
+projections and decode are measured after it the same way and reported under `other_workloads` (--also).
 
 Prints ONE JSON line.  `value` is the step's GEMM work divided by the whole step time (TFLOP/s), so the
-quantizers' time counts against it; the timed region is K back-to-back steps between two synchronizations,
-after an untimed settle phase (the step repeated for --settle-ms, reported as settle_steps) and W warmup
-steps.
+quantizers' and the routing's time counts against it; the timed region is K back-to-back steps between two
+synchronizations, after an untimed settle phase (the step repeated for --settle-ms, reported as
+settle_steps) and W warmup steps.
 The GEMM's own duration is measured inside that region with a HIP event pair around each of its launches,
 recorded on the stream the kernels are launched on; the quantizers' durations come from a second pass of K
 steps with an event pair around every launch.  `roofline` describes the dominant kernel (the GEMM) against
@@ -600,32 +603,12 @@ def profiled_traffic(kname, workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="up", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--settle-ms", type=float, default=2500.0,
-                    help="before the warmup steps, repeat the step for this long (untimed) so that the GPU's "
-                         "clocks reach their sustained state; the count is reported as settle_steps")
-    ap.add_argument("--pmc-copy-mb", type=int, default=0,
-                    help="before warmup, run one plain elementwise copy (torch.neg) of this many MiB; its "
-                         "FETCH_SIZE / WRITE_SIZE under rocprofv3 calibrate the traffic counters")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built and measured for a "
-              f"single MI355X.", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args, he, copy_gbs):
+    """Settle, warm up and time `args.steps` steps of workload `name`; returns its part of the JSON line (without
+    the CPU baseline) and the Workload."""
     import torch
 
-    import fine_grained_quantization_amd as fq
-
-    fq.load_library()  # fails loudly when the HIP library is missing
-    torch.cuda.set_device(0)
-    wk = Workload(args.workload)
+    wk = Workload(name)
     if args.pmc_copy_mb:
         src = torch.ones(args.pmc_copy_mb << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -648,9 +631,8 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, back to back, between two synchronizations; an event pair brackets
-    # every GEMM launch in it.
+    # every launch of the step's last (dominant) kernel in it.
     nk = len(wk.kernels)
-    he = HipEvents()
     gemm_raw = [(he.create(), he.create()) for _ in range(args.steps)]
     gemm_ev = [[_Rec(he, a), _Rec(he, b)] for a, b in gemm_raw]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -670,7 +652,7 @@ def main():
         he.destroy(a)
         he.destroy(b)
 
-    # Quantizer durations: K more steps with an event pair around every launch.
+    # The other kernels' durations: K more steps with an event pair around every launch.
     raw = [[(he.create(), he.create()) for _ in range(nk)] for _ in range(args.steps)]
     for s in range(args.steps):
         wk.step([[_Rec(he, a), _Rec(he, b)] for a, b in raw[s]])
@@ -690,6 +672,7 @@ def main():
             info["frac_fp8_peak"] = round(work["flops"] / us / 1e6 / PEAK_FP8_TFLOPS, 4)
         info["GB/s"] = round(work["bytes"] / us / 1e3, 1)
         info["frac_hbm"] = round(work["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4)
+        info["frac_of_measured_copy"] = round(work["bytes"] / us / 1e3 / copy_gbs, 4)
         kernels[kname] = info
 
     for pairs in raw:
@@ -698,18 +681,14 @@ def main():
             he.destroy(b)
     gname, _, gwork = wk.kernels[-1]
     g = kernels[gname]
-    traffic = profiled_traffic(gname, args.workload)
-    if args.workload in BANDWIDTH_METRICS:
-        roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
-    elif args.workload == "decode":
+    traffic = profiled_traffic(gname, name)
+    if name in BANDWIDTH_METRICS or name == "decode":
         roof = {"kernel": gname, "bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(g["GB/s"] / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"kernel": gname, "bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
     roof["algorithmic_bytes"] = int(gwork["bytes"])
-    copy_gbs = measured_copy_gbs()
     roof["measured_copy_GBs"] = round(copy_gbs, 1)
     if roof["bound"] == "hbm":
         roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
@@ -722,16 +701,89 @@ def main():
         roof["peak_at_measured_clock"] = round(at_clock, 1)
         roof["frac_at_measured_clock"] = round(roof["achieved"] / at_clock, 4)
 
+    dq = name in BANDWIDTH_METRICS
+    part = {
+        "value": round(wk.bytes / (ms_step * 1e-3) / 1e9, 1) if dq else round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "GB/s" if dq else "TFLOP/s",
+        "settle_steps": settle_steps,
+        "ms_per_step": round(ms_step, 4),
+        "config": {"workload": DESCRIPTIONS[name], "name": name, "M": wk.M, "N": wk.N, "K": wk.K, "out": "bf16",
+                   "parallelism": "single GPU"},
+        "kernels": kernels,
+        "roofline": roof,
+        "wall_s_timed": round(wall, 3),
+        "gpu_clock": clk,
+    }
+    if name == "moe":
+        part["config"]["rows_used"] = wk.rows_used   # M is the routing capacity the buffers are sized to
+    return part, wk
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moe", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the headline one, each reported under "
+                         "other_workloads with its own step time, kernels and roofline (default: up,down,decode "
+                         "with the moe headline, none otherwise; 'none' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=2500.0,
+                    help="before the warmup steps, repeat the step for this long (untimed) so that the GPU's "
+                         "clocks reach their sustained state; the count is reported as settle_steps")
+    ap.add_argument("--pmc-copy-mb", type=int, default=0,
+                    help="before warmup, run one plain elementwise copy (torch.neg) of this many MiB; its "
+                         "FETCH_SIZE / WRITE_SIZE under rocprofv3 calibrate the traffic counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built and measured for a "
+              f"single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.also is None:
+        also = ["up", "down", "decode"] if args.workload == "moe" else []
+    else:
+        also = [] if args.also in ("", "none") else args.also.split(",")
+    for a in also:
+        if a not in DESCRIPTIONS or a == args.workload:
+            print(f"--also: {a!r} is not another workload", file=sys.stderr)
+            sys.exit(2)
+
+    import torch
+
+    import fine_grained_quantization_amd as fq
+
+    fq.load_library()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    he = HipEvents()
+    copy_gbs = measured_copy_gbs()
+    part, wk = measure(args.workload, args, he, copy_gbs)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wk)
+        cpu["cpu_model"] = cpu_model()
+    del wk
+    others = {}
+    for a in also:
+        torch.cuda.empty_cache()
+        p, w = measure(a, args, he, copy_gbs)
+        del w
+        others[a] = {k: p[k] for k in ("value", "unit", "ms_per_step", "settle_steps", "config", "kernels",
+                                       "roofline", "gpu_clock")}
+        log(f"[bench] {a}: {p['ms_per_step']} ms per step")
+
     dq = args.workload in BANDWIDTH_METRICS
     out = {
         "metric": BANDWIDTH_METRICS[args.workload] if dq else METRIC,
-        "value": round(wk.bytes / (ms_step * 1e-3) / 1e9, 1) if dq else round(wk.flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "GB/s" if dq else "TFLOP/s",
+        "value": part["value"],
+        "unit": part["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle_steps": settle_steps,
-        "ms_per_step": round(ms_step, 4),
+        "settle_steps": part["settle_steps"],
+        "ms_per_step": part["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -739,19 +791,16 @@ def main():
                   "per_channel": "bf16 -> fp8_e4m3", "e5m6": "bf16 -> e5m6"}.get(
             args.workload, "fp8_e4m3"),
         "data": "synthetic",
-        "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload, "M": wk.M, "N": wk.N,
-                   "K": wk.K, "out": "bf16", "parallelism": "single GPU"},
-        "kernels": kernels,
-        "roofline": roof,
-        "wall_s_timed": round(wall, 3),
-        "gpu_clock": clk,
+        "config": part["config"],
+        "kernels": part["kernels"],
+        "roofline": part["roofline"],
+        "wall_s_timed": part["wall_s_timed"],
+        "gpu_clock": part["gpu_clock"],
     }
-    if args.workload == "moe":
-        out["config"]["rows_used"] = wk.rows_used   # M is the routing capacity the buffers are sized to
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wk)
-        out["cpu_baseline"]["cpu_model"] = cpu_model()
+    if others:
+        out["other_workloads"] = others
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

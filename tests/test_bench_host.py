@@ -58,3 +58,12 @@ def test_sampler_start_and_stop_do_not_block():
     r = s.record(0.0, 1e18)
     assert isinstance(r["windows"], int)
     assert "error" not in r or (isinstance(r["error"], str) and r["error"])
+
+
+def test_also_rejects_unknown_or_repeated_workloads():
+    """--also names other workloads; an unknown name, or the headline itself, is refused before any GPU
+    work."""
+    for also in ("nosuch", "moe"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--also", also], capture_output=True,
+                           text=True, timeout=120)
+        assert r.returncode == 2 and "--also" in r.stderr and r.stdout == ""
