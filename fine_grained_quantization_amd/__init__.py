@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     fp8q_moe_gather_fp8,
     fp8q_moe_route_capacity,
     fp8q_moe_route_topk,
+    fp8q_moe_route_topk_noalloc,
     fp8q_quant_act_1x128,
     fp8q_quant_act_dual,
     fp8q_quant_act_e5m6_1x128,

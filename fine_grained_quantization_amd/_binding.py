@@ -48,12 +48,13 @@ def load_library(path: str = LIB_PATH):
         lib.fp8q_grouped_gemm_blockscaled_gather.argtypes = [P, P, I64, P, P, P, P, I, P, I64, I64, I64, I64, P]
         lib.fp8q_moe_route_topk.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, P]
         lib.fp8q_moe_gather_fp8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, I64, P, P, P]
+        lib.fp8q_moe_route_topk_noalloc.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
         for f in (lib.fp8q_quant_act_1x128, lib.fp8q_quant_w_128x128, lib.fp8q_swiglu_quant_act_1x128,
                   lib.fp8q_swiglu_bf16, lib.fp8q_quant_act_dual, lib.fp8q_quant_act_fp4_1x128,
                   lib.fp8q_quant_w_fp4_128x128, lib.fp8q_quant_w_per_channel, lib.fp8q_quant_act_e5m6_1x128,
                   lib.fp8q_gemm_blockscaled,
                   lib.fp8q_grouped_gemm_blockscaled, lib.fp8q_grouped_gemm_blockscaled_gather,
-                  lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk,
+                  lib.fp8q_dequant_w_128x128, lib.fp8q_moe_route_topk, lib.fp8q_moe_route_topk_noalloc,
                   lib.fp8q_moe_gather_fp8):
             f.restype = ctypes.c_int
         lib.fp8q_moe_route_capacity.argtypes = [I64, I64, I64]
@@ -442,6 +443,31 @@ def fp8q_moe_route_topk(logits, k: int, rows: int | None = None, workspace=None,
                                    _ptr(row_token), rows, _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "fp8q_moe_route_topk")
+    return topk_idx, offsets, row_of, row_token
+
+
+def fp8q_moe_route_topk_noalloc(logits, k: int, rows: int | None = None, out=None, stream=None):
+    """:func:`fp8q_moe_route_topk` through the entry point that allocates nothing: its workspace is the
+    library's fixed per-GPU array (calls that overlap on one GPU race).  ``out`` (the four outputs) is
+    allocated here when not given; the C call itself allocates nothing."""
+    _need(logits, "logits", (torch.float32,), 2)
+    T, E = logits.shape
+    lib = load_library()
+    cap = fp8q_moe_route_capacity(T, E, k)
+    rows = cap if rows is None else rows
+    if out is None:
+        dev = logits.device
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty(rows, dtype=torch.int32, device=dev))
+    topk_idx, offsets, row_of, row_token = out
+    for t, n, size in ((topk_idx, "topk_idx", T * k), (offsets, "offsets", E + 1), (row_of, "row_of", T * k),
+                       (row_token, "row_token", rows)):
+        _need(t, n, (torch.int32,))
+        if t.numel() != size:
+            raise ValueError(f"{n} has {t.numel()} elements; expected {size}")
+    _check(lib.fp8q_moe_route_topk_noalloc(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
+                                           _ptr(row_token), rows, _stream_ptr(stream)),
+           "fp8q_moe_route_topk_noalloc")
     return topk_idx, offsets, row_of, row_token
 
 

@@ -42,6 +42,8 @@ constexpr int64_t kMaxK = int64_t(1) << 23;  // GEMM tiles address 256 rows of K
 
 int finish(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
+static_assert(fp8q::kRouteScratchBytes == FP8Q_MOE_ROUTE_NOALLOC_BYTES, "the header states the array's size");
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +259,29 @@ int fp8q_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t k, in
     if (rc) return rc;
     return finish(fp8q::launch_moe_route_topk(logits, T, (int)E, (int)k, topk_idx, offsets, row_of, row_token, rows,
                                               static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int fp8q_moe_route_topk_noalloc(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_idx,
+                                int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows, void *stream) {
+    const int64_t cap = fp8q_moe_route_capacity(T, E, k);
+    if (cap < 0 || rows < cap || rows > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;
+    if (!offsets || !row_token) return FP8Q_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !row_of)) return FP8Q_ERR_NULL;
+    if (!aligned4(offsets) || !aligned4(row_token) ||
+        (T > 0 && (!aligned4(logits) || !aligned4(topk_idx) || !aligned4(row_of))))
+        return FP8Q_ERR_ALIGN;
+    if (fp8q::moe_route_workspace_bytes(T, E) > fp8q::kRouteScratchBytes) return FP8Q_ERR_WORKSPACE;
+    int rc = check_device();
+    if (rc) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return FP8Q_ERR_NO_DEVICE;
+    }
+    int32_t *ws = nullptr;
+    if (fp8q::route_scratch(dev, &ws) != hipSuccess) return FP8Q_ERR_HIP;
+    return finish(fp8q::launch_moe_route_topk(logits, T, (int)E, (int)k, topk_idx, offsets, row_of, row_token, rows,
+                                              ws, static_cast<hipStream_t>(stream)));
 }
 
 int fp8q_moe_gather_fp8(const uint8_t *q, const float *s, int64_t T, int64_t K, int64_t k, const int32_t *row_of,

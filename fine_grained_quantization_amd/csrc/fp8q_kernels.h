@@ -38,6 +38,11 @@ hipError_t launch_grouped_gemm_gather(const uint8_t *q, const float *s, int64_t 
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeMaxK = 16;
 int64_t moe_route_workspace_bytes(int64_t T, int64_t E);
+// Bytes of the routing's fixed device workspace (one per GPU) used by the entry point that allocates nothing.
+constexpr int64_t kRouteScratchBytes = int64_t(4) << 20;
+// Device address of that workspace on device `dev`, which must be the current device (looked up on the first
+// call per device, then cached).
+hipError_t route_scratch(int dev, int32_t **ptr);
 hipError_t launch_moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
                                  int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows,
                                  int32_t *workspace, hipStream_t stream);

@@ -21,7 +21,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fp8q_kernels.h"
+
+// The routing's workspace for callers that cannot allocate: a file-scope device array of a fixed size, which
+// each GPU the library runs on holds until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is only a stand-in): its device address is looked up once per device with
+// hipGetSymbolAddress and that address is used instead.
+static __device__ __align__(256) int32_t scratch[fp8q::kRouteScratchBytes / 4];
 
 namespace fp8q {
 namespace {
@@ -289,6 +298,35 @@ __global__ __launch_bounds__(256) void moe_gather_fp8_kernel(const uint8_t *__re
 }  // namespace
 
 int64_t moe_route_workspace_bytes(int64_t T, int64_t E) { return (T + kChunk - 1) / kChunk * E * 4; }
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<int32_t *> g_scratch[kScratchDevices];
+std::mutex g_scratch_lock;
+}  // namespace
+
+hipError_t route_scratch(int dev, int32_t **ptr) {
+    *ptr = nullptr;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    int32_t *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> g(g_scratch_lock);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            // `dev` is the current device (the caller checked), so this is that device's copy of the array.
+            void *a = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || a == nullptr) {
+                (void)hipGetLastError();
+                return e != hipSuccess ? e : hipErrorInvalidSymbol;
+            }
+            p = static_cast<int32_t *>(a);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_moe_route_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
                                  int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows,

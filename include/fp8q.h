@@ -289,6 +289,28 @@ int fp8q_moe_route_topk(const float *logits, int64_t T, int64_t E, int64_t k, in
                         int32_t *row_of, int32_t *row_token, int64_t rows, void *workspace, int64_t workspace_bytes,
                         void *stream);
 
+/* fp8q_moe_route_topk for callers that cannot allocate device memory (code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same outputs, bit for bit, with the workspace taken from a
+ * fixed array inside the library instead of from the caller.  The array holds
+ * FP8Q_MOE_ROUTE_NOALLOC_BYTES bytes on each GPU the library runs on and is
+ * kept until the process ends; its device address is looked up on the first
+ * call on each device.  This call allocates and frees nothing.
+ *   logits, topk_idx, offsets, row_of, row_token, rows : as fp8q_moe_route_topk
+ * Requires what fp8q_moe_route_topk requires (without its workspace
+ * arguments), and fp8q_moe_route_workspace_bytes(T, E) <=
+ * FP8Q_MOE_ROUTE_NOALLOC_BYTES (4 * E * ceil(T / 64) <= 4 MiB: for example
+ * up to 65536 tokens over 1024 experts, or 262144 tokens over 256); larger
+ * calls return FP8Q_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (concurrent streams, or threads without ordering between their streams)
+ * race and give unspecified outputs; calls ordered on one stream are safe.  The
+ * array needs no clearing: every entry a call reads was written earlier in the
+ * same call.  Returns FP8Q_ERR_HIP if the array's address cannot be obtained. */
+#define FP8Q_MOE_ROUTE_NOALLOC_BYTES (4 * 1024 * 1024)
+int fp8q_moe_route_topk_noalloc(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *topk_idx,
+                                int32_t *offsets, int32_t *row_of, int32_t *row_token, int64_t rows, void *stream);
+
 /* Expert-sorted FP8 activations for the grouped GEMM (FP8 dispatch): for every
  * row r < min(offsets[E], rows),
  *   qa[r, :] = q[row_token[r], :],  sa[kb][r] = s[kb][row_token[r]]

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
               "fp8q_moe_route_workspace_bytes", "fp8q_moe_route_topk", "fp8q_moe_gather_fp8",
               "fp8q_swiglu_quant_act_1x128", "fp8q_swiglu_bf16", "fp8q_quant_act_dual",
               "fp8q_quant_act_fp4_1x128", "fp8q_quant_w_fp4_128x128", "fp8q_quant_w_per_channel",
-              "fp8q_quant_act_e5m6_1x128", "fp8q_grouped_gemm_blockscaled_gather", "fp8q_status_string", "fp8q_version"):
+              "fp8q_quant_act_e5m6_1x128", "fp8q_grouped_gemm_blockscaled_gather", "fp8q_moe_route_topk_noalloc",
+              "fp8q_status_string", "fp8q_version"):
         assert n in names
 
 
@@ -156,6 +157,15 @@ def test_moe_routing_sizes_and_validation(lib):
     assert route(A, 100, 8, 2, A, A, A, A, cap, None, 4096, None) == -1
     assert route(MIS, 100, 8, 2, A, A, A, A, cap, A, 4096, None) == -3
     assert route(A, 100, 8, 2, A, A, A, A, cap, A, 4 * 8 * 2 - 1, None) == -8    # workspace too small
+    na = lib.fp8q_moe_route_topk_noalloc
+    na.argtypes = [ctypes.c_void_p, I, I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, I,
+                   ctypes.c_void_p]
+    assert na(A, 100, 8, 9, A, A, A, A, cap, None) == -2                           # k > E
+    assert na(A, 100, 8, 2, A, A, A, A, cap - 1, None) == -2                       # rows below the capacity
+    assert na(A, 100, 8, 2, A, None, A, A, cap, None) == -1
+    assert na(MIS, 100, 8, 2, A, A, A, A, cap, None) == -3
+    big_t = 65536 + 64                                                             # 4 * 1024 * 1025 bytes > 4 MiB
+    assert na(A, big_t, 1024, 2, A, A, A, A, lib.fp8q_moe_route_capacity(big_t, 1024, 2), None) == -8
     gather = lib.fp8q_moe_gather_fp8
     gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, I, I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                        I, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
