@@ -54,3 +54,33 @@ def test_calls_follow_their_stream():
     assert torch.equal(qa, qa0) and torch.equal(sa.view(torch.int32), sa0.view(torch.int32))
     assert torch.equal(qw, qw0) and torch.equal(sw.view(torch.int32), sw0.view(torch.int32))
     assert torch.equal(c.view(torch.int16), c0.view(torch.int16))
+
+
+def test_benchmark_moe_step_on_two_streams_matches_one_stream():
+    """The benchmark's MoE step runs the token quantization and the routing on a second stream beside the
+    weight quantization, and the GEMM waits for both.  Several steps back to back (a step's token
+    quantization must not overwrite tokens the previous step's GEMM still reads) give, bit for bit, the
+    outputs of the same calls made one after another on one stream."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    wk = bench.Workload("moe")
+    assert wk.side is not None
+    say("moe step on two streams, 4 steps back to back")
+    for _ in range(4):
+        wk.step()
+    torch.cuda.synchronize()
+    outs = [t.clone() for t in (wk.qt, wk.st, *wk.route_out, wk.qw, wk.sw, wk.c)]
+    # the same kernels in order on the current stream alone
+    for t in (wk.qt, wk.qw, wk.c, *wk.route_out):
+        t.zero_()
+    wk.st.zero_()
+    wk.sw.zero_()
+    for _, fn, _ in wk.kernels:
+        fn()
+    torch.cuda.synchronize()
+    refs = (wk.qt, wk.st, *wk.route_out, wk.qw, wk.sw, wk.c)
+    for i, (a, b) in enumerate(zip(outs, refs)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"output {i} differs"
