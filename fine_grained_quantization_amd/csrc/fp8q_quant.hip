@@ -144,38 +144,53 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
 // Forward and backward FP8 copies of a Linear input in one pass (page "The Definitive Information To
 // Deepseek", the passage on caching the Linear's input in FP8 for the backward pass).  The backward pass
 // contracts the input over tokens (the weight gradient dW = dY^T x), so its copy is the 1x128 quantization
-// of x^T: one scale per channel and 128 tokens, stored channel-major.  A workgroup (256 threads) owns 128
-// tokens x 128 channels; thread t holds 8 consecutive tokens (8 (t / 16) ...) x 8 consecutive channels
-// (chunk t % 16), 8 loads of 16 bytes (a wave's load instruction covers 4 rows x 256 bytes).
-//  - forward copy: a token's 128 channels lie in the 16 lanes of one DPP row (8 row maxima per thread);
-//  - backward copy: a channel's 128 tokens lie in 16 threads spread over the 4 waves; their maxima over
-//    8 rows go through LDS, and each thread stores its 8 tokens' codes of each of its channels (8 bytes).
+// of x^T: one scale per channel and 128 tokens, stored channel-major.  A workgroup (512 threads, 8 waves)
+// owns 128 tokens x 128 channels; thread t holds 4 consecutive tokens (4 (t / 16) ...) x 8 consecutive
+// channels (chunk t % 16), 4 loads of 16 bytes (a wave's load instruction covers 4 rows x 256 bytes).
+//  - forward copy: a token's 128 channels lie in the 16 lanes of one DPP row (4 row maxima per thread);
+//    the 128 token scales leave as one run of 512 bytes;
+//  - backward copy: a channel's 128 tokens lie in 16 threads spread over the 8 waves; their maxima over 4
+//    rows go through LDS, one thread per channel forms the scale and its reciprocal, and the codes are
+//    transposed through an LDS tile [128 channels][128 tokens] so that they leave as whole 128-byte rows
+//    of the channel-major copy (16 bytes per lane) rather than as 4-byte pieces.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_at(const u32x4 &v, int c) {
     const uint32_t d = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
     return (c & 1) ? bf16_hi(d) : bf16_lo(d);
 }
 
-__global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K,
-                                                             uint8_t *__restrict__ q, float *__restrict__ s,
-                                                             uint8_t *__restrict__ qt, float *__restrict__ st) {
-    __shared__ float colmax[16][128];
-    __shared__ float colscale[128];
+constexpr int kDualThreads = 512;
+
+__global__ __launch_bounds__(kDualThreads) void quant_act_dual_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                                      int64_t K, uint8_t *__restrict__ q,
+                                                                      float *__restrict__ s, uint8_t *__restrict__ qt,
+                                                                      float *__restrict__ st) {
+    constexpr int R = 4;                       // tokens per thread
+    constexpr int G = kDualThreads / 16;       // token groups of R
+    // colmax: per-group channel maxima, dead once the channel scales are formed; the code tile reuses it.
+    // Tile row = channel, 128 code bytes = 8 pieces of 16 bytes; piece p of row r sits at p ^ ((r / 8) & 7),
+    // which spreads one store instruction's 4-byte writes over the LDS banks.
+    __shared__ __align__(16) union {
+        float colmax[G][128];
+        uint32_t tile[128 * 32];
+    } sh;
+    __shared__ double colinv[128];
+    __shared__ float rowsc[128];
     const int t = threadIdx.x;
     const int64_t KB = K >> 7;
     const int64_t kb = (int64_t)blockIdx.x % KB;
     const int64_t mb = (int64_t)blockIdx.x / KB;
     const int chunk = t & 15, g = t >> 4;
-    const int64_t m0 = mb * 128 + g * 8;
+    const int64_t m0 = mb * 128 + g * R;
     const int64_t c0 = kb * 128 + chunk * 8;
 
-    u32x4 v[8];
+    u32x4 v[R];
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = load_stream16(x + (m0 + j) * K + c0);
+    for (int j = 0; j < R; j++) v[j] = load_stream16(x + (m0 + j) * K + c0);
 
     // forward: per token, 128 channels
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int j = 0; j < R; j++) {
         float amax = 0.0f;
         amax = absmax2(amax, v[j].x);
         amax = absmax2(amax, v[j].y);
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
         o.x = quant4(v[j].x, v[j].y, inv);
         o.y = quant4(v[j].z, v[j].w, inv);
         *reinterpret_cast<uint2 *>(q + (m0 + j) * K + c0) = o;
-        if (chunk == 0) s[kb * M + m0 + j] = sc;
+        if (chunk == 0) rowsc[g * R + j] = sc;
     }
 
     // backward: per channel, 128 tokens
@@ -196,28 +211,39 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
     for (int c = 0; c < 8; c++) {
         float cm = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) cm = fmaxf(cm, fabsf(bf16_at(v[j], c)));
-        colmax[g][chunk * 8 + c] = cm;
+        for (int j = 0; j < R; j++) cm = fmaxf(cm, fabsf(bf16_at(v[j], c)));
+        sh.colmax[g][chunk * 8 + c] = cm;
     }
     __syncthreads();
+    float csc = 0.0f;
     if (t < 128) {
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; i++) amax = fmaxf(amax, colmax[i][t]);
-        const float sc = group_scale(amax);
-        colscale[t] = sc;
-        st[mb * K + kb * 128 + t] = sc;
+        for (int i = 0; i < G; i++) amax = fmaxf(amax, sh.colmax[i][t]);
+        csc = group_scale(amax);
+        colinv[t] = scale_reciprocal(csc);
+    }
+    __syncthreads();
+    if (t < 128) {
+        st[mb * K + kb * 128 + t] = csc;
+        s[kb * M + mb * 128 + t] = rowsc[t];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        const double inv = colinv[chunk * 8 + c];
+        const int row = chunk * 8 + c;
+        const uint32_t w = encode4(quotient(bf16_at(v[0], c), inv), quotient(bf16_at(v[1], c), inv),
+                                   quotient(bf16_at(v[2], c), inv), quotient(bf16_at(v[3], c), inv));
+        // token bytes 4g..4g+3 are word g of the row: piece g / 4, word g % 4 within it
+        sh.tile[row * 32 + (((g >> 2) ^ (chunk & 7)) << 2) + (g & 3)] = w;
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; c++) {
-        const double inv = scale_reciprocal(colscale[chunk * 8 + c]);
-        uint2 o;
-        o.x = encode4(quotient(bf16_at(v[0], c), inv), quotient(bf16_at(v[1], c), inv),
-                      quotient(bf16_at(v[2], c), inv), quotient(bf16_at(v[3], c), inv));
-        o.y = encode4(quotient(bf16_at(v[4], c), inv), quotient(bf16_at(v[5], c), inv),
-                      quotient(bf16_at(v[6], c), inv), quotient(bf16_at(v[7], c), inv));
-        *reinterpret_cast<uint2 *>(qt + (c0 + c) * M + m0) = o;
+    for (int i = 0; i < 1024 / kDualThreads; i++) {
+        const int p = t + i * kDualThreads;  // 16-byte piece p % 8 of channel row p / 8
+        const int row = p >> 3, piece = p & 7;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(&sh.tile[row * 32 + ((piece ^ ((row >> 3) & 7)) << 2)]);
+        *reinterpret_cast<u32x4 *>(qt + (kb * 128 + row) * M + mb * 128 + piece * 16) = w;
     }
 }
 
@@ -577,7 +603,7 @@ hipError_t launch_swiglu_quant_act_1x128(const uint16_t *x, const uint16_t *y, i
 hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
                                  float *st, hipStream_t stream) {
     const int64_t blocks = (M / 128) * (K / 128);
-    quant_act_dual_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, M, K, q, s, qt, st);
+    quant_act_dual_kernel<<<dim3((unsigned)blocks), kDualThreads, 0, stream>>>(x, M, K, q, s, qt, st);
     return hipGetLastError();
 }
 
