@@ -126,7 +126,7 @@ int fp8q_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q
     if (N == 0) return FP8Q_OK;
     if (!s || (K > 0 && (!w || !q))) return FP8Q_ERR_NULL;  // K == 0: only the (zero) scales are written
     if (!aligned4(s) || (K > 0 && (!aligned16(w) || !aligned16(q)))) return FP8Q_ERR_ALIGN;
-    if ((N + 3) / 4 > kMaxGrid) return FP8Q_ERR_SHAPE;
+    if (N > kMaxGrid) return FP8Q_ERR_SHAPE;  // one workgroup per row
     int rc = check_device();
     if (rc) return rc;
     return finish(fp8q::launch_quant_w_per_channel(w, N, K, q, s, static_cast<hipStream_t>(stream)));

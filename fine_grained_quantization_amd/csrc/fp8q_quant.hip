@@ -447,56 +447,59 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 // ---------------------------------------------------------------------------------------------
 // Per-channel FP8 weights (page "DeepSeek starts updating frequently", the TileKernels quantization modes:
 // per token, per block, per channel).  Read as one scale per output channel: row n of W [N, K] over all of
-// K, s[n] = fl32(amax_n / 448), the codes as in the grouped modes.  One wave per row (4 rows a workgroup),
-// so the row's max-abs is a wave reduction with no LDS or barrier.  Lane l holds the row's 16-byte chunks
-// l, l + 64, ...: the first kRowChunks of them stay in registers between the max and the encode (rows up
-// to 64 * kRowChunks * 8 = 8192 elements are read once); chunks past them are read again for the encode
-// (from L2: the row was just read).  Each load and store instruction of a wave is contiguous.
+// K, s[n] = fl32(amax_n / 448), the codes as in the grouped modes.  One workgroup (4 waves) per row: thread
+// t holds the row's 16-byte chunks t, t + 256, ..., the first CH of them in registers between the max and
+// the encode (rows up to 256 * CH * 8 elements are read once); chunks past them are read twice, the second
+// time from the cache (the row was just read).  The row's max-abs is a wave reduction and a 4-entry LDS
+// exchange.  Every load and store instruction of a wave is contiguous.  Four waves per row rather than one
+// keep 4 chunks a lane in registers for a 7168-element row (50 VGPRs, 8 waves per SIMD) instead of 14 (166
+// VGPRs, 3 waves per SIMD), so more rows are in flight while others encode.
 // ---------------------------------------------------------------------------------------------
-constexpr int kRowChunks = 16;
-
-__global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t *__restrict__ w, int64_t N,
-                                                                  int64_t K, uint8_t *__restrict__ q,
-                                                                  float *__restrict__ s) {
-    const int lane = threadIdx.x & 63;
-    const int64_t n = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (n >= N) return;  // whole waves leave
+template <int CH>
+__global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t *__restrict__ w, int64_t K,
+                                                                  uint8_t *__restrict__ q, float *__restrict__ s) {
+    __shared__ float wmax[4];
+    const int t = threadIdx.x;
+    const int64_t n = blockIdx.x;
     const int64_t chunks = K >> 3;
     const uint16_t *row = w + n * K;
     uint8_t *dst = q + n * K;
 
-    u32x4 v[kRowChunks];
+    u32x4 v[CH];
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kRowChunks; j++) {
-        const int64_t c = lane + 64 * j;
+    for (int j = 0; j < CH; j++) {
+        const int64_t c = t + 256 * j;
         v[j] = c < chunks ? load_stream16(row + c * 8) : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < kRowChunks; j++) {
+    for (int j = 0; j < CH; j++) {
         amax = absmax2(amax, v[j].x);
         amax = absmax2(amax, v[j].y);
         amax = absmax2(amax, v[j].z);
         amax = absmax2(amax, v[j].w);
     }
-    for (int64_t c = lane + 64 * kRowChunks; c < chunks; c += 64) {
-        const u32x4 t = *reinterpret_cast<const u32x4 *>(row + c * 8);
-        amax = absmax2(absmax2(absmax2(absmax2(amax, t.x), t.y), t.z), t.w);
+    for (int64_t c = t + 256 * CH; c < chunks; c += 256) {
+        const u32x4 u = *reinterpret_cast<const u32x4 *>(row + c * 8);  // cached: read again below
+        amax = absmax2(absmax2(absmax2(absmax2(amax, u.x), u.y), u.z), u.w);
     }
     amax = wave_max(amax);
+    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float sc = group_scale(amax);
     const double inv = scale_reciprocal(sc);
 #pragma unroll
-    for (int j = 0; j < kRowChunks; j++) {
-        const int64_t c = lane + 64 * j;
+    for (int j = 0; j < CH; j++) {
+        const int64_t c = t + 256 * j;
         if (c < chunks)
             *reinterpret_cast<uint2 *>(dst + c * 8) = (uint2){quant4(v[j].x, v[j].y, inv), quant4(v[j].z, v[j].w, inv)};
     }
-    for (int64_t c = lane + 64 * kRowChunks; c < chunks; c += 64) {
-        const u32x4 t = load_stream16(row + c * 8);
-        *reinterpret_cast<uint2 *>(dst + c * 8) = (uint2){quant4(t.x, t.y, inv), quant4(t.z, t.w, inv)};
+    for (int64_t c = t + 256 * CH; c < chunks; c += 256) {
+        const u32x4 u = load_stream16(row + c * 8);
+        *reinterpret_cast<uint2 *>(dst + c * 8) = (uint2){quant4(u.x, u.y, inv), quant4(u.z, u.w, inv)};
     }
-    if (lane == 0) s[n] = sc;
+    if (t == 0) s[n] = sc;
 }
 
 // FP8 -> BF16 weight conversion with 128x128 block scales (page "deepseek-ai/DeepSeek-V3", "How to Run
@@ -587,8 +590,14 @@ hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, u
 
 hipError_t launch_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                       hipStream_t stream) {
-    const int64_t blocks = (N + 3) / 4;  // one wave per row
-    quant_w_per_channel_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(w, N, K, q, s);
+    // one workgroup per row; chunks a lane keeps in registers: 4 for rows up to 8192 elements, else 8 (rows
+    // past 16384 elements read the rest twice; holding 12 a lane measured slower at 18432, as its 130 VGPRs
+    // leave 3 waves per SIMD)
+    const dim3 grid((unsigned)N);
+    if (K <= 256 * 4 * 8)
+        quant_w_per_channel_kernel<4><<<grid, 256, 0, stream>>>(w, K, q, s);
+    else
+        quant_w_per_channel_kernel<8><<<grid, 256, 0, stream>>>(w, K, q, s);
     return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 """GPU parity of the per-channel FP8 weight quantization (one scale per output channel over the whole row)
-with the oracle, bit-exact: ragged row counts and lengths, rows longer than the part a wave keeps in
-registers, special values, the up projection's full weight, and the K = 128 case against the 1x128
-quantizer."""
+with the oracle, bit-exact: ragged row counts and lengths, rows longer than the part a workgroup keeps in
+registers (8192 elements, 16384 for longer rows; the rest is read twice), special values, the up
+projection's full weight, and the K = 128 case against the 1x128 quantizer."""
 import numpy as np
 import pytest
 import torch
@@ -45,9 +45,19 @@ def check(wb, what):
 
 
 @pytest.mark.parametrize("N,K", [(37, 1000), (1, 8), (5, 8192), (6, 8200), (130, 24576), (300, 7168),
-                                 (4, 0), (3, 136)])
+                                 (4, 0), (3, 136), (9, 16384), (7, 16392)])
 def test_matches_oracle(N, K):
     check(rows_of(np.random.default_rng([51, N, K]), N, K), "ragged")
+
+
+def test_row_maximum_in_the_twice_read_tail():
+    """Rows longer than the part a workgroup keeps in registers (16384 elements): the maximum in the chunks that
+    are read twice (the last element, or the first chunk past the registers), or in the registers."""
+    wb = rows_of(np.random.default_rng(53), 8, 20480)
+    wb[3, -1] = 0x4800            # 131072, the row's maximum, in its last element
+    wb[4, 16384] = 0xC800         # -131072, the first element past the registers
+    wb[5, 16383] = 0x4800         # the last element held in registers
+    check(wb, "maximum in the tail")
 
 
 def test_up_projection_weight():
