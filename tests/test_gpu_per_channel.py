@@ -64,6 +64,12 @@ def test_up_projection_weight():
     check(wl.per_channel()["w"], "up projection weight")
 
 
+def test_down_projection_weight():
+    """The down projection's weight [7168, 18432] (the down workload's recipe and seed): rows past 16384
+    elements, so each workgroup keeps 8 chunks a lane in registers and reads the rest twice."""
+    check(wl.normal_bf16(wl.SEEDS["down"], wl.T_W, (7168, 18432), 0.02), "down projection weight")
+
+
 def test_k128_equals_the_1x128_quantizer():
     wb = rows_of(np.random.default_rng(52), 64, 128)
     q1, s1 = fq.fp8q_quant_w_per_channel(bf16_dev(wb))
