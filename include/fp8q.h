@@ -113,11 +113,12 @@ int fp8q_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *
  * 4-byte aligned s; with K == 0, w and q may be null and s is set to 0. */
 int fp8q_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s, void *stream);
 
-/* Forward and backward FP8 copies of a Linear input in one pass (the passage
- * on caching the Linear's input in FP8 for the backward pass).  The backward
- * pass contracts the input over tokens (dW = dY^T x), so its FP8 copy needs
- * groups along tokens; this library reads it as the 1x128 quantization of x^T
- * (one scale per channel and 128 tokens), made from the same bf16 x:
+/* Forward and backward FP8 copies of a Linear input in one pass (page "The
+ * Definitive Information To Deepseek", the passage on caching the Linear's
+ * input in FP8 for the backward pass).  The backward pass contracts the input
+ * over tokens (dW = dY^T x), so its FP8 copy needs groups along tokens; this
+ * library reads it as the 1x128 quantization of x^T (one scale per channel and
+ * 128 tokens), made from the same bf16 x:
  *   x  : bf16 [M, K]            (input)
  *   q  : E4M3 [M, K], s : fp32 [K/128][M]     (output: exactly fp8q_quant_act_1x128)
  *   qt : E4M3 [K, M] (channel-major), st : fp32 [M/128][K]   (output)
