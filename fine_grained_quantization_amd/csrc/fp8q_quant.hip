@@ -110,12 +110,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        float amax = 0.0f;
-        amax = absmax2(amax, v[j].x);
-        amax = absmax2(amax, v[j].y);
-        amax = absmax2(amax, v[j].z);
-        amax = absmax2(amax, v[j].w);
-        amax = row16_max(amax);
+        const float amax = bf16_mag_f32(row16_max(absmax_bits(v[j])));
         const float sc = FMT == kFmtFp4 ? group_scale_fp4(amax)
                          : FMT == kFmtE5M6 ? group_scale_e5m6(amax) : group_scale(amax);
         const double inv = scale_reciprocal(sc);
@@ -165,13 +160,13 @@ __global__ __launch_bounds__(kDualThreads) void quant_act_dual_kernel(const uint
                                                                       int64_t K, uint8_t *__restrict__ q,
                                                                       float *__restrict__ s, uint8_t *__restrict__ qt,
                                                                       float *__restrict__ st) {
-    constexpr int R = 4;                       // tokens per thread
+    constexpr int R = 4;                       // tokens per thread (the column maxima below take 4)
     constexpr int G = kDualThreads / 16;       // token groups of R
     // colmax: per-group channel maxima, dead once the channel scales are formed; the code tile reuses it.
     // Tile row = channel, 128 code bytes = 8 pieces of 16 bytes; piece p of row r sits at p ^ ((r / 8) & 7),
     // which spreads one store instruction's 4-byte writes over the LDS banks.
     __shared__ __align__(16) union {
-        float colmax[G][128];
+        uint32_t colmax[G][128];   // magnitude bit patterns
         uint32_t tile[128 * 32];
     } sh;
     __shared__ double colinv[128];
@@ -191,12 +186,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_act_dual_kernel(const uint
     // forward: per token, 128 channels
 #pragma unroll
     for (int j = 0; j < R; j++) {
-        float amax = 0.0f;
-        amax = absmax2(amax, v[j].x);
-        amax = absmax2(amax, v[j].y);
-        amax = absmax2(amax, v[j].z);
-        amax = absmax2(amax, v[j].w);
-        amax = row16_max(amax);
+        const float amax = bf16_mag_f32(row16_max(absmax_bits(v[j])));
         const float sc = group_scale(amax);
         const double inv = scale_reciprocal(sc);
         uint2 o;
@@ -206,21 +196,24 @@ __global__ __launch_bounds__(kDualThreads) void quant_act_dual_kernel(const uint
         if (chunk == 0) rowsc[g * R + j] = sc;
     }
 
-    // backward: per channel, 128 tokens
+    // backward: per channel, 128 tokens.  Channels 2d and 2d + 1 of the chunk share dword d of every token's
+    // load, so one packed maximum over the R tokens gives both channels' magnitude maxima.
+    {
+        const u16x2 m[4] = {absmax_halves(v[0].x, v[1].x, v[2].x, v[3].x), absmax_halves(v[0].y, v[1].y, v[2].y, v[3].y),
+                            absmax_halves(v[0].z, v[1].z, v[2].z, v[3].z), absmax_halves(v[0].w, v[1].w, v[2].w, v[3].w)};
 #pragma unroll
-    for (int c = 0; c < 8; c++) {
-        float cm = 0.0f;
-#pragma unroll
-        for (int j = 0; j < R; j++) cm = fmaxf(cm, fabsf(bf16_at(v[j], c)));
-        sh.colmax[g][chunk * 8 + c] = cm;
+        for (int d = 0; d < 4; d++) {
+            sh.colmax[g][chunk * 8 + 2 * d] = m[d].x;
+            sh.colmax[g][chunk * 8 + 2 * d + 1] = m[d].y;
+        }
     }
     __syncthreads();
     float csc = 0.0f;
     if (t < 128) {
-        float amax = 0.0f;
+        uint32_t amax = 0;
 #pragma unroll
-        for (int i = 0; i < G; i++) amax = fmaxf(amax, sh.colmax[i][t]);
-        csc = group_scale(amax);
+        for (int i = 0; i < G; i++) amax = max(amax, sh.colmax[i][t]);
+        csc = group_scale(bf16_mag_f32(amax));
         colinv[t] = scale_reciprocal(csc);
     }
     __syncthreads();
@@ -348,12 +341,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_act_1x128_kernel(const uint1
         h.y = swiglu_bf16x2(vx[j].y, vy[j].y);
         h.z = swiglu_bf16x2(vx[j].z, vy[j].z);
         h.w = swiglu_bf16x2(vx[j].w, vy[j].w);
-        float amax = 0.0f;
-        amax = absmax2(amax, h.x);
-        amax = absmax2(amax, h.y);
-        amax = absmax2(amax, h.z);
-        amax = absmax2(amax, h.w);
-        amax = row16_max(amax);
+        const float amax = bf16_mag_f32(row16_max(absmax_bits(h)));
         const float sc = group_scale(amax);
         const double inv = scale_reciprocal(sc);
         const int64_t m = row0 + j;
@@ -396,7 +384,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <bool FP4, bool STREAM_OUT = false>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w, int64_t K,
                                                               uint8_t *__restrict__ q, float *__restrict__ s) {
-    __shared__ float wave_amax[4];
+    __shared__ uint32_t wave_amax[4];
     const int tid = threadIdx.x;
     const int64_t KB = K >> 7;
     const int64_t kb = (int64_t)blockIdx.x % KB;
@@ -409,18 +397,13 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 #pragma unroll
     for (int i = 0; i < 8; i++) v[i] = load_stream16(base + (int64_t)(r0 + 16 * i) * K);
 
-    float amax = 0.0f;
+    u16x2 mh = absmax_halves(v[0]);
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        amax = absmax2(amax, v[i].x);
-        amax = absmax2(amax, v[i].y);
-        amax = absmax2(amax, v[i].z);
-        amax = absmax2(amax, v[i].w);
-    }
-    amax = wave_max(amax);
-    if ((tid & 63) == 0) wave_amax[tid >> 6] = amax;
+    for (int i = 1; i < 8; i++) mh = __builtin_elementwise_max(mh, absmax_halves(v[i]));
+    const uint32_t wm = wave_max(halves_max(mh));
+    if ((tid & 63) == 0) wave_amax[tid >> 6] = wm;
     __syncthreads();
-    amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
+    const float amax = bf16_mag_f32(max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3])));
     const float sc = FP4 ? group_scale_fp4(amax) : group_scale(amax);
     const double inv = scale_reciprocal(sc);
 
@@ -458,7 +441,7 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 template <int CH>
 __global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t *__restrict__ w, int64_t K,
                                                                   uint8_t *__restrict__ q, float *__restrict__ s) {
-    __shared__ float wmax[4];
+    __shared__ uint32_t wmax[4];
     const int t = threadIdx.x;
     const int64_t n = blockIdx.x;
     const int64_t chunks = K >> 3;
@@ -466,28 +449,22 @@ __global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t
     uint8_t *dst = q + n * K;
 
     u32x4 v[CH];
-    float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < CH; j++) {
         const int64_t c = t + 256 * j;
         v[j] = c < chunks ? load_stream16(row + c * 8) : (u32x4){0u, 0u, 0u, 0u};
     }
+    u16x2 mh = absmax_halves(v[0]);
 #pragma unroll
-    for (int j = 0; j < CH; j++) {
-        amax = absmax2(amax, v[j].x);
-        amax = absmax2(amax, v[j].y);
-        amax = absmax2(amax, v[j].z);
-        amax = absmax2(amax, v[j].w);
-    }
+    for (int j = 1; j < CH; j++) mh = __builtin_elementwise_max(mh, absmax_halves(v[j]));
     for (int64_t c = t + 256 * CH; c < chunks; c += 256) {
         const u32x4 u = *reinterpret_cast<const u32x4 *>(row + c * 8);  // cached: read again below
-        amax = absmax2(absmax2(absmax2(absmax2(amax, u.x), u.y), u.z), u.w);
+        mh = __builtin_elementwise_max(mh, absmax_halves(u));
     }
-    amax = wave_max(amax);
-    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    const uint32_t wm = wave_max(halves_max(mh));
+    if ((t & 63) == 0) wmax[t >> 6] = wm;
     __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float sc = group_scale(amax);
+    const float sc = group_scale(bf16_mag_f32(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))));
     const double inv = scale_reciprocal(sc);
 #pragma unroll
     for (int j = 0; j < CH; j++) {
@@ -568,6 +545,11 @@ hipError_t launch_quant_act_e5m6_1x128(const uint16_t *x, int64_t M, int64_t K, 
     return hipGetLastError();
 }
 
+// Dynamic LDS the weight quantizers reserve (and do not use) so that at most 4 workgroups share a CU's
+// 160 KB: at 64 VGPRs 8 would fit, and with 8 blocks of 128 rows each per CU in flight the kernel measured
+// 1.5-3% slower than with 4 (up weight 65.2 vs 63.8 us, the MoE layer's 64 experts 502 vs 486 us).
+constexpr size_t kWeightQuantLds = 36 * 1024;
+
 hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                   hipStream_t stream) {
     const int64_t blocks = (N / 128) * (K / 128);  // 1-D grid: K-block fastest
@@ -575,16 +557,16 @@ hipError_t launch_quant_w_128x128(const uint16_t *w, int64_t N, int64_t K, uint8
     // (132 MB of codes, which the GEMM after it reads from the Infinity Cache) 63.5 -> 67 us, so only codes
     // larger than the cache stream.
     if (N * K > (int64_t(256) << 20))
-        quant_w_128x128_kernel<false, true><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+        quant_w_128x128_kernel<false, true><<<dim3((unsigned)blocks), 256, kWeightQuantLds, stream>>>(w, K, q, s);
     else
-        quant_w_128x128_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+        quant_w_128x128_kernel<false><<<dim3((unsigned)blocks), 256, kWeightQuantLds, stream>>>(w, K, q, s);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                       hipStream_t stream) {
     const int64_t blocks = (N / 128) * (K / 128);
-    quant_w_128x128_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(w, K, q, s);
+    quant_w_128x128_kernel<true><<<dim3((unsigned)blocks), 256, kWeightQuantLds, stream>>>(w, K, q, s);
     return hipGetLastError();
 }
 
