@@ -64,3 +64,19 @@ def assert_gemm_within_bound(gpu: np.ndarray, C: np.ndarray, B: np.ndarray, bf16
 def literal_bound_ratio(gpu: np.ndarray, C: np.ndarray, B: np.ndarray) -> float:
     """max |gpu - C| / (1e-3 B + 1e-6): the literal bound, reported for bf16 outputs too."""
     return float(np.max(np.abs(gpu - C) / (1e-3 * B + 1e-6))) if gpu.size else 0.0
+
+
+def every_amax_groups(seed, limit=0x7F80):
+    """One 128-element group per positive finite bf16 amax pattern below `limit` (denormals included): the amax
+    at a random position with a random sign, the other 127 elements random bf16 patterns of magnitude <= amax
+    with random signs.  Returns the groups as rows of 8 groups ([ceil(n / 8), 1024] bf16 bits, zero-padded)."""
+    g = np.random.default_rng(seed)
+    amax = np.arange(1, limit, dtype=np.uint16)
+    n = len(amax)
+    lim = amax.astype(np.int64)
+    rest = np.minimum((g.random((n, 127)) * (lim[:, None] + 1)).astype(np.int64), lim[:, None]).astype(np.uint16)
+    rest |= (g.random((n, 127)) < 0.5).astype(np.uint16) << 15
+    rows = np.concatenate([amax[:, None] | ((g.random((n, 1)) < 0.5).astype(np.uint16) << 15), rest], axis=1)
+    rows = np.take_along_axis(rows, np.argsort(g.random((n, 128)), axis=1), axis=1)
+    rows = np.concatenate([rows, np.zeros(((-n) % 8, 128), np.uint16)])
+    return rows.reshape(-1, 1024)

@@ -6,7 +6,7 @@ import pytest
 import fine_grained_quantization_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import bf16_dev, host, say
+from gpu_util import bf16_dev, every_amax_groups, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,3 +42,15 @@ def test_scaled_channels_and_special_values(M, K):
     xb[sub] = g.integers(1, 0x80, sub.sum()).astype(np.uint16) | (g.integers(0, 2, sub.sum()) << 15).astype(np.uint16)
     say(f"dual quant: M={M} K={K}")
     check(xb, f"{M}x{K}")
+
+
+def test_every_amax_for_both_copies():
+    """Every positive finite bf16 amax as the maximum of a channel's 128 tokens (the backward copy's groups: the
+    groups of every_amax_groups laid out as columns), which also gives the forward groups (one token, 128
+    channels) maxima all over the range."""
+    cols = every_amax_groups(85).reshape(-1, 128)        # one 128-element group per row
+    n = (len(cols) + 127) // 128 * 128                    # whole K-blocks of channels
+    cols = np.concatenate([cols, np.zeros((n - len(cols), 128), np.uint16)])
+    xb = np.ascontiguousarray(cols.T)                     # [128 tokens, n channels]
+    say(f"dual quant: every amax as a channel maximum, {xb.shape}")
+    check(xb, "every amax")

@@ -8,7 +8,7 @@ import pytest
 import fine_grained_quantization_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import bf16_dev, host, say
+from gpu_util import bf16_dev, every_amax_groups, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,11 @@ def test_every_bf16_value_at_scale_one():
     head = np.full((vals.shape[0], 1), wl.bf16_bits(np.array([65024.0], np.float32))[0], np.uint16)
     x = np.concatenate([head, vals], axis=1).reshape(-1, 1024)
     check(x, "every bf16 value at scale 1")
+
+
+def test_every_amax():
+    """One group per positive finite bf16 amax: every scale fl32(amax / 65024) the quantizer can form."""
+    check(every_amax_groups(84), "every bf16 amax")
 
 
 @pytest.mark.parametrize("M,K", [(37, 640), (1, 128), (16, 512), (300, 1152)])

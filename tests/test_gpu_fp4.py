@@ -6,7 +6,7 @@ import pytest
 import fine_grained_quantization_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import bf16_dev, host, say
+from gpu_util import bf16_dev, every_amax_groups, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,14 @@ def test_activations_up_input():
     say(f"fp4 act: up input {d['a'].shape}")
     q, s = fq.fp8q_quant_act_fp4_1x128(bf16_dev(d["a"]))
     same(host(q), host(s), *oracle.quant_act_fp4_1x128(d["a"]), "up input")
+
+
+def test_activations_every_amax():
+    """One group per positive finite bf16 amax: every scale fl32(amax / 6) the activation quantizer can form."""
+    xb = every_amax_groups(83)
+    say(f"fp4 act: every bf16 amax, {xb.shape}")
+    q, s = fq.fp8q_quant_act_fp4_1x128(bf16_dev(xb))
+    same(host(q), host(s), *oracle.quant_act_fp4_1x128(xb), "every amax")
 
 
 @pytest.mark.parametrize("M,K", [(37, 640), (1, 128), (300, 1024)])
