@@ -435,8 +435,8 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 // the encode (rows up to 256 * CH * 8 elements are read once); chunks past them are read twice, the second
 // time from the cache (the row was just read).  The row's max-abs is a wave reduction and a 4-entry LDS
 // exchange.  Every load and store instruction of a wave is contiguous.  Four waves per row rather than one
-// keep 4 chunks a lane in registers for a 7168-element row (50 VGPRs, 8 waves per SIMD) instead of 14 (166
-// VGPRs, 3 waves per SIMD), so more rows are in flight while others encode.
+// keep 4 chunks a lane in registers for a 7168-element row (under 64 VGPRs, 8 waves per SIMD) instead of 14
+// (over 128 VGPRs, 3 waves per SIMD), so more rows are in flight while others encode.
 // ---------------------------------------------------------------------------------------------
 template <int CH>
 __global__ __launch_bounds__(256) void quant_w_per_channel_kernel(const uint16_t *__restrict__ w, int64_t K,
@@ -573,8 +573,8 @@ hipError_t launch_quant_w_fp4_128x128(const uint16_t *w, int64_t N, int64_t K, u
 hipError_t launch_quant_w_per_channel(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *s,
                                       hipStream_t stream) {
     // one workgroup per row; chunks a lane keeps in registers: 4 for rows up to 8192 elements, else 8 (rows
-    // past 16384 elements read the rest twice).  Holding 12 a lane (130 VGPRs, 3 waves per SIMD) measured
-    // 10% slower at K = 18432 with the input still in the Infinity Cache and 7% faster with it evicted.
+    // past 16384 elements read the rest twice).  Holding 12 a lane (3 waves per SIMD when measured) ran 10%
+    // slower at K = 18432 with the input still in the Infinity Cache and 7% faster with it evicted.
     const dim3 grid((unsigned)N);
     if (K <= 256 * 4 * 8)
         quant_w_per_channel_kernel<4><<<grid, 256, 0, stream>>>(w, K, q, s);
