@@ -22,7 +22,9 @@ MI355X's published peaks; its `traffic` (HBM bytes per launch) is read from the 
 summary of that kernel and workload under profiles/, and is null when the kernel sources have changed since
 the counters were taken (the summary records their SHA-256).  `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.  Each kernel's entry gives the mean (the rates use it), median and
-minimum of its K launch durations.  `gpu_clock` is the graphics clock of each XCD while the steps ran (the
+minimum of its K launch durations; the 1x128 and 128x128 quantizers' entries add `torch_cast_floor`, the median
+duration of torch's own elementwise bf16 -> FP8 cast over the same input (the same bytes read and written,
+without max-abs or scales), a same-size floor for that quantizer on this GPU.  `gpu_clock` is the graphics clock of each XCD while the steps ran (the
 device's metrics table through amdsmi, about one refresh a second, hence the 2.5 s settle), and MFMA-bound
 lines add the FP8 peak at that clock.
 
@@ -109,6 +111,7 @@ class Workload:
 
         self.name = name
         self.side, self.side_kernels = None, ()
+        self.cast_floor = {}  # quantizer name -> its bf16 input, for the same-traffic torch cast floor
         dev = "cuda"
         t0 = time.time()
         d = wl.WORKLOADS[name]()
@@ -200,6 +203,9 @@ class Workload:
             kernels.append(("quant_w_128x128", lambda: fq.fp8q_quant_w_128x128(self.w, self.qw, self.sw),
                             {"bytes": w_bytes(wrows, K)}))
         self.c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.cast_floor = {"quant_act_1x128": self.a} if name != "down" else {}
+        if name != "decode":
+            self.cast_floor["quant_w_128x128"] = self.w
         self.flops = 2.0 * M * N * K
         kernels.append(("gemm_blockscaled",
                         lambda: fq.fp8q_gemm_blockscaled(self.qa, self.sa, self.qw, self.sw, c=self.c),
@@ -255,6 +261,7 @@ class Workload:
                                                              off, c=self.c),
              {"flops": self.flops, "bytes": gb}),
         ]
+        self.cast_floor = {"quant_act_1x128": self.tokens, "quant_w_128x128": self.w}
         # token quantization and routing (kernels 0 and 1) overlap the weight quantization (kernel 2)
         self.side, self.side_kernels = torch.cuda.Stream(), (0, 1)
         self.step_count = 0
@@ -313,6 +320,26 @@ def measured_copy_gbs(mib: int = 1024, reps: int = 5) -> float:
         best = min(best, a.elapsed_time(b))
     del src, dst
     return 2 * (mib << 20) / (best * 1e-3) / 1e9
+
+
+def cast_floor_us(src, reps: int) -> float:
+    """Median duration of torch's own elementwise bf16 -> float8_e4m3fn cast of `src` into a preallocated
+    tensor: it reads 2 and writes 1 byte per element, the traffic of a quantizer minus its scales (no max-abs,
+    no scale, one conversion per element), so it is a same-size floor for that quantizer on this GPU."""
+    import torch
+
+    dst = torch.empty(src.shape, dtype=torch.float8_e4m3fn, device=src.device)
+    each = []
+    for i in range(reps + 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            each.append(1e3 * a.elapsed_time(b))
+    del dst
+    return float(np.median(each))
 
 
 def cpu_model() -> str:
@@ -701,6 +728,13 @@ def measure(name, args, he, copy_gbs):
         info["GB/s"] = round(work["bytes"] / us / 1e3, 1)
         info["frac_hbm"] = round(work["bytes"] / us / 1e3 / PEAK_HBM_GBS, 4)
         info["frac_of_measured_copy"] = round(work["bytes"] / us / 1e3 / copy_gbs, 4)
+        if i in wk.side_kernels:
+            info["beside_weight_quant"] = True  # its duration includes waiting for CUs the weight quantizer holds
+        if kname in wk.cast_floor:
+            src = wk.cast_floor[kname]
+            fl = cast_floor_us(src, args.steps)
+            info["torch_cast_floor"] = {"us_median": round(fl, 2), "GB/s": round(3 * src.numel() / fl / 1e3, 1),
+                                        "frac_of_floor": round(fl / info["us_median"], 4)}
         kernels[kname] = info
 
     for pairs in raw:
