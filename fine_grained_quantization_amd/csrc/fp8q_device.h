@@ -116,6 +116,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
+// s_waitcnt immediate that waits until at most N vector memory loads of this wave are in flight, leaving
+// expcnt and lgkmcnt at their maxima (vmcnt is bits [3:0] and [15:14] of the immediate).
+template <int N>
+constexpr int vmcnt_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+}
+
 // Max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 within the row); every lane gets it.
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));

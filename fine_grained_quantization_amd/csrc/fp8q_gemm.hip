@@ -3,20 +3,19 @@
 // an fp32 accumulator (page "The Definitive Information To Deepseek": FP8 GEMM inputs with BF16/FP32
 // outputs; promotion of partial results alongside the MMA).
 //
-// Design:
+// Three kernels share the same arithmetic:
 //  * v_mfma_f32_16x16x128_f8f6f4 computes exactly one 128-deep K-block per instruction, so each
 //    MFMA result is one fresh partial sum P (C input = 0) and promotion is acc += P * (s_a * s_w).
 //  * Operand roles are swapped: the weight tile feeds the MFMA's row operand and the activation
 //    tile its column operand, so a lane's 4 result registers are 4 consecutive output channels of
 //    ONE token.  Every lane then promotes all its registers of a subtile with a single scalar
 //    s_a[kb][m] * s_w[n/128][kb], and stores 4 adjacent outputs with one instruction.
-//  * A workgroup tile is 128 tokens x 128 weight rows (the weight rows are exactly one scale
-//    block, so s_w is one scalar per K-block for the whole workgroup).  4 waves in a 2 x 2 grid,
-//    each 64 x 64 = 4 x 4 MFMA subtiles.  A and W K-block tiles (128 rows x 128 bytes) are staged
-//    through LDS, double-buffered, with a 16-byte-chunk XOR swizzle so that fragment reads are
-//    bank-conflict free.
-//  * The grouped (MoE) variant maps each 128-row M tile to the expert whose segment contains it
-//    (segments are multiples of 128 rows) and offsets the weight and scale pointers.
+//  * Operand tiles travel from global memory straight into LDS (buffer loads into LDS), rows stored
+//    with a 16-byte-chunk XOR swizzle so that fragment reads are bank-conflict free.
+// M > 128 runs the 256-row tile kernel (dense, grouped and gather-fused grouped); M <= 64 the small-M
+// kernel, whose waves split K; 64 < M <= 128 the mid-size kernel, whose waves split the tokens.  The
+// latter two give each CU one slice of weight rows, so the weights are streamed from HBM once.
+
 #include <atomic>
 
 #include "fp8q_device.h"
@@ -25,10 +24,6 @@
 namespace fp8q {
 
 namespace {
-
-constexpr int kBM = 128;            // tokens per workgroup tile
-constexpr int kBN = 128;            // weight rows per workgroup tile (one scale block)
-constexpr int kTile = 128 * 128;    // bytes of one operand tile for one K-block
 
 // LDS placement of a tile row: row r (128 bytes = 8 chunks of 16 bytes) stores logical chunk c at
 // physical chunk c ^ swzf(r).  Fragment reads touch 16 consecutive rows at one logical chunk; swzf is a
@@ -60,160 +55,6 @@ __device__ __forceinline__ void store4(void *c, int64_t idx, const v4f &v) {
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(c) + idx) = o;
     } else {
         *reinterpret_cast<float4 *>(static_cast<float *>(c) + idx) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-}
-
-template <bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(256, 2) void gemm_blockscaled_kernel(const uint8_t *__restrict__ qa,
-                                                                  const float *__restrict__ sa,
-                                                                  const uint8_t *__restrict__ qw,
-                                                                  const float *__restrict__ sw, void *__restrict__ c,
-                                                                  int64_t M, int64_t N, int64_t K,
-                                                                  const int32_t *__restrict__ off, int64_t E,
-                                                                  int64_t n_mtiles) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTile];  // [buffer][A tile | W tile]
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-    const int wn = wave & 1;   // which 64-row half of the weight tile
-    const int wm = wave >> 1;  // which 64-token half of the activation tile
-    const int64_t KB = K >> 7;
-    const int64_t mt = (int64_t)blockIdx.x % n_mtiles;
-    const int64_t nt = (int64_t)blockIdx.x / n_mtiles;
-    const int64_t m0 = mt * kBM;
-    const int64_t n0 = nt * kBN;
-
-    const uint8_t *W = qw;
-    const float *SW = sw;
-    if (GROUPED) {
-        int64_t e = -1;
-        for (int64_t i = 0; i < E; i++) {
-            if ((int64_t)off[i] <= m0 && m0 < (int64_t)off[i + 1]) {
-                e = i;
-                break;
-            }
-        }
-        if (e < 0) {  // no segment covers these rows: write zeros (only with offsets that break the rules)
-            const v4f z = {0.f, 0.f, 0.f, 0.f};
-            for (int i = tid; i < kBM * (kBN / 4); i += 256) {
-                const int64_t m = m0 + i / (kBN / 4);
-                const int64_t n = n0 + (i % (kBN / 4)) * 4;
-                store4<OUT_BF16>(c, m * N + n, z);
-            }
-            return;
-        }
-        W = qw + e * N * K;
-        SW = sw + e * (N / 128) * KB;
-    }
-
-    // Global -> LDS staging: thread tid moves 16-byte chunk (tid % 8) of tile rows tid / 8 + 32 i.
-    // Addresses are recomputed from scalars each time (arrays of pointers would live in scratch).
-    const int ch = tid & 7;
-    const int rr = tid >> 3;
-    const int64_t Mlast = M - 1;
-    const uint8_t *a_base = qa + ch * 16;
-    const uint8_t *w_base = W + (n0 + rr) * K + ch * 16;
-    // A row of staging slot i; the ragged M tail re-reads the last row (its outputs are not stored).
-#define FP8Q_AROW(i) ((m0 + rr + 32 * (i)) < M ? (m0 + rr + 32 * (i)) : Mlast)
-    // Token of this lane in subtile mi, clamped the same way for its scale.
-#define FP8Q_MROW(mi) ((m0 + wm * 64 + (mi) * 16 + (lane & 15)) < M ? (m0 + wm * 64 + (mi) * 16 + (lane & 15)) : Mlast)
-    const float *sw_row = SW + (n0 / 128) * KB;
-
-    v4f acc[4][4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ni++)
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) acc[ni][mi] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    u32x4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3;
-#define FP8Q_LOAD_TILES(koff)                                                                        \
-    do {                                                                                             \
-        ra0 = *reinterpret_cast<const u32x4 *>(a_base + FP8Q_AROW(0) * K + (koff));                 \
-        ra1 = *reinterpret_cast<const u32x4 *>(a_base + FP8Q_AROW(1) * K + (koff));                 \
-        ra2 = *reinterpret_cast<const u32x4 *>(a_base + FP8Q_AROW(2) * K + (koff));                 \
-        ra3 = *reinterpret_cast<const u32x4 *>(a_base + FP8Q_AROW(3) * K + (koff));                 \
-        rw0 = *reinterpret_cast<const u32x4 *>(w_base + (koff));                                    \
-        rw1 = *reinterpret_cast<const u32x4 *>(w_base + 32 * K + (koff));                           \
-        rw2 = *reinterpret_cast<const u32x4 *>(w_base + 64 * K + (koff));                           \
-        rw3 = *reinterpret_cast<const u32x4 *>(w_base + 96 * K + (koff));                           \
-    } while (0)
-#define FP8Q_STORE_TILES(dst)                                                                        \
-    do {                                                                                             \
-        *reinterpret_cast<u32x4 *>((dst) + swz(rr, ch)) = ra0;                                       \
-        *reinterpret_cast<u32x4 *>((dst) + swz(rr + 32, ch)) = ra1;                                  \
-        *reinterpret_cast<u32x4 *>((dst) + swz(rr + 64, ch)) = ra2;                                  \
-        *reinterpret_cast<u32x4 *>((dst) + swz(rr + 96, ch)) = ra3;                                  \
-        *reinterpret_cast<u32x4 *>((dst) + kTile + swz(rr, ch)) = rw0;                               \
-        *reinterpret_cast<u32x4 *>((dst) + kTile + swz(rr + 32, ch)) = rw1;                          \
-        *reinterpret_cast<u32x4 *>((dst) + kTile + swz(rr + 64, ch)) = rw2;                          \
-        *reinterpret_cast<u32x4 *>((dst) + kTile + swz(rr + 96, ch)) = rw3;                          \
-    } while (0)
-
-    FP8Q_LOAD_TILES(0);
-    FP8Q_STORE_TILES(lds);
-    float sa_cur[4], sa_nxt[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa[FP8Q_MROW(mi)];
-    float sw_cur = sw_row[0], sw_nxt = 0.f;
-    __syncthreads();
-
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t kb = 0; kb < KB; kb++) {
-        const int buf = (int)(kb & 1);
-        const bool more = kb + 1 < KB;
-        if (more) {
-            FP8Q_LOAD_TILES((kb + 1) * 128);
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++) sa_nxt[mi] = sa[(kb + 1) * M + FP8Q_MROW(mi)];
-            sw_nxt = sw_row[kb + 1];
-        }
-
-        const uint8_t *tA = lds + buf * 2 * kTile;
-        const uint8_t *tW = tA + kTile;
-        v8i wf[4], af[4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ni++) wf[ni] = load_frag(tW, wn * 64 + ni * 16, lane);
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) af[mi] = load_frag(tA, wm * 64 + mi * 16, lane);
-        v4f p[4][4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ni++)
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++) p[ni][mi] = mfma_fp8_16x16x128(wf[ni], af[mi], zero);
-        float cs[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) cs[mi] = sa_cur[mi] * sw_cur;
-#pragma unroll
-        for (int ni = 0; ni < 4; ni++)
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) acc[ni][mi][r] = __builtin_fmaf(p[ni][mi][r], cs[mi], acc[ni][mi][r]);
-
-        if (more) {
-            FP8Q_STORE_TILES(lds + (buf ^ 1) * 2 * kTile);
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sa_nxt[mi];
-            sw_cur = sw_nxt;
-        }
-        __syncthreads();
-    }
-#undef FP8Q_LOAD_TILES
-#undef FP8Q_STORE_TILES
-#undef FP8Q_AROW
-
-    // Epilogue: lane holds C[m][n .. n+3] for each subtile.
-#undef FP8Q_MROW
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++) {
-        const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
-        if (m < M) {
-#pragma unroll
-            for (int ni = 0; ni < 4; ni++) {
-                const int64_t n = n0 + wn * 64 + ni * 16 + 4 * (lane >> 4);
-                store4<OUT_BF16>(c, m * N + n, acc[ni][mi]);
-            }
-        }
     }
 }
 
@@ -872,8 +713,10 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
         for (int j = 0; j < 8; j++)
             fp8q_raw_buffer_load_lds(ta, (__attribute__((address_space(3))) void *)(aslot + j * 1024), 16, a_voff[j],
                                      so, 0, 0);
-        fp8q_raw_buffer_load_lds(ts, (__attribute__((address_space(3))) void *)(aslot + kA), 4, lane * 4,
-                                 in ? kb * (int)M * 4 : 0, 0, 0);
+        // (the K-block's offset in the per-lane offset, which the hardware range-checks: tokens past M in the
+        // last K-block then read zeros; the scalar offset is not range-checked)
+        fp8q_raw_buffer_load_lds(ts, (__attribute__((address_space(3))) void *)(aslot + kA), 4,
+                                 lane * 4 + (in ? kb * (int)M * 4 : 0), 0, 0, 0);
         fp8q_raw_buffer_load_lds(tsw, (__attribute__((address_space(3))) void *)(aslot + kA + 256), 4, sw_voff,
                                  in ? kb * 4 : 0, 0, 0);
     };
@@ -941,6 +784,139 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
     }
 }
 
+// =============================================================================================
+// Mid-size M kernel (64 < M <= 128): as in the small-M kernel, the N rows are dealt out in slices of R rows (one
+// slice per CU, R <= 80), so the weight matrix is streamed from HBM exactly once by all CUs; here every
+// workgroup holds all 128 token rows, and the 8 waves split the tokens instead of K: wave w owns token subtile w
+// (16 tokens) and all NSUB weight subtiles, so each output has one owner and no partial sums are exchanged.  The
+// K-blocks flow through a ring of kMidStages LDS stages shared by the waves: each stage holds a K-block's weight
+// rows, its 128 token rows and their scales, copied with buffer loads straight into LDS (rows past the slice or
+// past M read zeros), and the copies run kMidStages - 1 K-blocks ahead of the MFMAs.  Every wave issues the same
+// kMidCopies copy instructions per K-block, so the number of its loads still in flight is the same constant
+// every iteration: where a wave has nothing to copy, it loads through a zero-byte resource into a scratch area
+// of LDS that nothing reads (a load into LDS that is out of range still writes its zeros).
+// =============================================================================================
+
+constexpr int kMidM = 128;
+constexpr int kMidStages = 5;  // 5 x (10 KB weight + 16 KB tokens + 768 B scales) + 1 KB = 135 KB of LDS
+constexpr int kMidCopies = 5;  // copy instructions per wave per K-block: 2 token groups, 2 weight groups, 1 scale
+
+template <bool OUT_BF16, int NSUB>
+__global__ __launch_bounds__(512, 1) void gemm_midm_kernel(const uint8_t *__restrict__ qa,
+                                                           const float *__restrict__ sa,
+                                                           const uint8_t *__restrict__ qw,
+                                                           const float *__restrict__ sw, void *__restrict__ c,
+                                                           int64_t M, int64_t N, int64_t K, int64_t rows_per_wg) {
+    constexpr int kW = NSUB * 16 * 128;   // weight rows of one K-block
+    constexpr int kA = kMidM * 128;       // token rows of one K-block
+    constexpr int kSa = kW + kA;          // 128 token scales
+    constexpr int kSw = kSa + kMidM * 4;  // weight scales of blocks nb0, nb0 + 1 (64 slots)
+    constexpr int kStage = kSw + 256;
+    constexpr int kDummy = kMidStages * kStage;  // 1 KB that absorbs the zeros of the loads with nothing to copy
+    static_assert(2 * NSUB <= 16, "at most 16 weight row groups");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDummy + 1024];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
+    const int KB = (int)(K >> 7);
+    const int64_t n0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t nrows = (N - n0) < rows_per_wg ? (N - n0) : rows_per_wg;
+
+    const i32x4 rw = make_rsrc(qw + n0 * K, (uint64_t)nrows * (uint64_t)K);
+    const i32x4 rA = make_rsrc(qa, (uint64_t)M * (uint64_t)K);
+    const i32x4 rS = make_rsrc(sa, (uint64_t)M * (uint64_t)KB * 4);
+    const int64_t nb0 = n0 / 128;
+    const i32x4 rSW = make_rsrc(sw, (uint64_t)(N / 128) * (uint64_t)KB * 4);
+
+    // Copy assignment.  Row groups of 8 rows (1 KB, one instruction): lane l lands in row 8 j + l / 8, physical
+    // chunk l % 8, which holds logical chunk (l % 8) ^ swzf(row).  Wave w copies token groups w and w + 8, weight
+    // groups w and w + 8 (when they exist), and one scale dword per lane: waves 0 and 1 the token scales of
+    // tokens [64 w, 64 w + 64), wave 2 the weight scales of blocks nb0 and nb0 + 1 (lanes 0 and 1).
+    const int rsub = lane >> 3;
+    int voff[2];  // rows 8 (w + 8 j) + l / 8 of either operand
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int r = 8 * (wave + 8 * j) + rsub;
+        voff[j] = r * (int)K + (((lane & 7) ^ swzf(r)) << 4);
+    }
+    const bool has_w0 = wave < 2 * NSUB, has_w1 = wave + 8 < 2 * NSUB;  // wave-uniform
+    const int64_t nbl = nb0 + lane < N / 128 - 1 ? nb0 + lane : N / 128 - 1;
+    const int sc_voff = wave < 2 ? (wave * 64 + lane) * 4 : (lane < 2 ? (int)(nbl * KB * 4) : kOutOfRange);
+    const int sc_lds = wave < 2 ? kSa + wave * 256 : kSw;
+    int sw_idx[NSUB];  // weight-scale slot (0 or 1) of this lane's 4 rows 16 ns + 4 (lane / 16) .. +3
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ns++) {
+        int64_t nb = (n0 + ns * 16 + 4 * (lane >> 4)) / 128;
+        nb = nb < N / 128 ? nb : N / 128 - 1;
+        sw_idx[ns] = (int)(nb - nb0);
+    }
+
+    // Copies of K-block kb into its stage; past the last K-block (kb >= KB, wave-uniform) every resource has zero
+    // bytes, so the loads read zeros without touching memory (and still count as issued loads).
+    auto issue = [&](int kb) {
+        uint8_t *st = lds + (kb % kMidStages) * kStage;
+        const bool in = kb < KB;
+        const int so = in ? kb * 128 : 0;
+        const i32x4 ta = in ? rA : empty_rsrc(rA);
+        const i32x4 tw0 = in && has_w0 ? rw : empty_rsrc(rw), tw1 = in && has_w1 ? rw : empty_rsrc(rw);
+        // Token scales: the K-block's offset goes into the per-lane offset, which the hardware range-checks, so
+        // tokens past M in the last K-block read zeros (the scalar offset is not range-checked).
+        const i32x4 ts = !in ? empty_rsrc(rS) : (wave < 2 ? rS : (wave == 2 ? rSW : empty_rsrc(rSW)));
+        const int svo = wave < 2 && in ? sc_voff + kb * (int)M * 4 : sc_voff;
+        const int sso = wave == 2 && in ? kb * 4 : 0;
+        fp8q_raw_buffer_load_lds(ta, (lds_ptr)(st + kW + wave * 1024), 16, voff[0], so, 0, 0);
+        fp8q_raw_buffer_load_lds(ta, (lds_ptr)(st + kW + (wave + 8) * 1024), 16, voff[1], so, 0, 0);
+        fp8q_raw_buffer_load_lds(tw0, (lds_ptr)(has_w0 ? st + wave * 1024 : lds + kDummy), 16, voff[0], so, 0, 0);
+        fp8q_raw_buffer_load_lds(tw1, (lds_ptr)(has_w1 ? st + (wave + 8) * 1024 : lds + kDummy), 16, voff[1], so, 0,
+                                 0);
+        fp8q_raw_buffer_load_lds(ts, (lds_ptr)(wave <= 2 ? st + sc_lds : lds + kDummy), 4, svo, sso, 0, 0);
+    };
+
+    v4f acc[NSUB];
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ns++) acc[ns] = (v4f){0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < kMidStages - 1; s++) issue(s);
+    for (int kb = 0; kb < KB; kb++) {
+        // This wave's copies of K-block kb have landed (those of the next kMidStages - 2 may still be in flight);
+        // after the barrier every wave's have, and every wave is done with the stage K-block kb - 1 used.  (A
+        // plain s_barrier: __syncthreads would also wait for every load in flight.  The stage's data was written
+        // by the loads, and every read of the freed stage has returned, as its MFMAs and products consumed it.)
+        __builtin_amdgcn_s_waitcnt(vmcnt_le<(kMidStages - 2) * kMidCopies>());
+        __builtin_amdgcn_s_barrier();
+        issue(kb + kMidStages - 1);
+        const uint8_t *st = lds + (kb % kMidStages) * kStage;
+        const float *ssc = reinterpret_cast<const float *>(st + kSa);
+        const float *wsc = reinterpret_cast<const float *>(st + kSw);
+        const v8i af = load_frag(st + kW, wave * 16, lane);
+        v8i wf[NSUB];
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ns++) wf[ns] = load_frag(st, ns * 16, lane);
+        const float s_tok = ssc[wave * 16 + (lane & 15)];
+        const float sw0 = wsc[0], sw1 = wsc[1];
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ns++) {
+            const v4f p = mfma_fp8_16x16x128(wf[ns], af, zero);
+            const float cs = s_tok * (sw_idx[ns] ? sw1 : sw0);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[ns][r] = __builtin_fmaf(p[r], cs, acc[ns][r]);
+        }
+    }
+    // Lane holds C[m][n .. n+3] of each subtile, m = 16 wave + lane % 16, n = 16 ns + 4 (lane / 16) within the
+    // slice; rows n are all in or all out of the slice.
+    __builtin_amdgcn_s_waitcnt(0);  // the last (zero-byte) copies have retired before the workgroup ends
+    const int64_t m = wave * 16 + (lane & 15);
+    if (m < M) {
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ns++) {
+            const int nl = ns * 16 + 4 * (lane >> 4);
+            if (nl < nrows) store4<OUT_BF16>(c, m * N + n0 + nl, acc[ns]);
+        }
+    }
+}
+
 int cu_count() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
@@ -980,17 +956,27 @@ hipError_t launch_smallm(const uint8_t *qa, const float *sa, const uint8_t *qw, 
     return hipGetLastError();
 }
 
-template <bool GROUPED>
-hipError_t launch(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, bool out_bf16,
-                  int64_t M, int64_t N, int64_t K, const int32_t *off, int64_t E, hipStream_t stream) {
-    const int64_t n_mtiles = (M + kBM - 1) / kBM;
-    const int64_t blocks = n_mtiles * (N / kBN);
-    if (out_bf16)
-        gemm_blockscaled_kernel<true, GROUPED>
-            <<<dim3((unsigned)blocks), 256, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles);
-    else
-        gemm_blockscaled_kernel<false, GROUPED>
-            <<<dim3((unsigned)blocks), 256, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, off, E, n_mtiles);
+template <bool OUT_BF16>
+hipError_t launch_midm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream) {
+    // The small-M kernel's slices: a multiple of 8 rows giving about one slice per CU, at most 5 subtiles.
+    const int64_t ncu = cu_count();
+    int64_t rows = 8 * ((N / 8 + ncu - 1) / ncu);
+    rows = rows < 16 * kDecMaxSub ? rows : 16 * kDecMaxSub;
+    const int nsub = (int)((rows + 15) / 16);
+    const dim3 grid((unsigned)((N + rows - 1) / rows));
+    switch (nsub) {
+#define FP8Q_MIDM_CASE(S)                                                                                  \
+    case S:                                                                                                \
+        gemm_midm_kernel<OUT_BF16, S><<<grid, 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, rows);         \
+        break;
+        FP8Q_MIDM_CASE(1)
+        FP8Q_MIDM_CASE(2)
+        FP8Q_MIDM_CASE(3)
+        FP8Q_MIDM_CASE(4)
+        FP8Q_MIDM_CASE(5)
+#undef FP8Q_MIDM_CASE
+    }
     return hipGetLastError();
 }
 
@@ -1004,7 +990,8 @@ int64_t grouped_gemm_blocks(int64_t M, int64_t N, int64_t E) {
 }
 
 int64_t gemm_blocks(int64_t M, int64_t N) {
-    return ((M + kBM - 1) / kBM) * (N / kBN) + 8 * 1024;  // generous upper bound over both kernels
+    // an upper bound over the kernels: 256 x 128 tiles at the narrowest, or one workgroup per 8 weight rows
+    return ((M + kBig - 1) / kBig) * ((N + 127) / 128) + 256 + (N + 7) / 8;
 }
 
 hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c,
@@ -1012,7 +999,9 @@ hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uin
     if (M <= kSmallM)
         return out_bf16 ? launch_smallm<true>(qa, sa, qw, sw, c, M, N, K, stream)
                         : launch_smallm<false>(qa, sa, qw, sw, c, M, N, K, stream);
-    if (M <= 128) return launch<false>(qa, sa, qw, sw, c, out_bf16, M, N, K, nullptr, 0, stream);
+    if (M <= kMidM)
+        return out_bf16 ? launch_midm<true>(qa, sa, qw, sw, c, M, N, K, stream)
+                        : launch_midm<false>(qa, sa, qw, sw, c, M, N, K, stream);
     return out_bf16 ? launch_256<true>(qa, sa, qw, sw, c, M, N, K, stream)
                     : launch_256<false>(qa, sa, qw, sw, c, M, N, K, stream);
 }

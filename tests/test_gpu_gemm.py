@@ -256,6 +256,40 @@ def test_decode_small_m_full_size(out):
     say(f"  max err/bound {r:.3g}; literal-bound ratio {literal_bound_ratio(c, C, B):.3g}")
 
 
+# N -> slice rows as for the small-M kernel; the mid-size-M kernel (64 < M <= 128) takes every token row in one
+# workgroup: 256 -> 8 rows (NSUB 1), 4352 -> 24 (2), 8320 -> 40 (3), 12416 -> 56 (4), 18432 -> 72 (5).  K = 128
+# and 384 leave fewer K-blocks than the copies run ahead.
+@pytest.mark.parametrize("M,N,K,out", [(65, 256, 384, "f32"), (128, 4352, 384, "bf16"), (96, 8320, 128, "f32"),
+                                       (100, 12416, 384, "bf16"), (127, 18432, 640, "f32"), (128, 18432, 256, "bf16")])
+def test_mid_m_slice_widths(M, N, K, out):
+    """Every subtile count of the mid-size-M kernel, ragged token counts and short K."""
+    g = np.random.default_rng([67, M, N, K])
+    a = g.standard_normal((M, K)).astype(np.float32)
+    a *= np.exp2(g.integers(-6, 7, size=(M, 1))).astype(np.float32)
+    ab = wl.bf16_bits(a)
+    wb = wl.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say(f"gemm: mid-size M={M} N={N} K={K} out={out}")
+    c = gemm_out_to_f64(gpu_path(ab, wb, out))
+    C, B = oracle_path(ab, wb)
+    assert_gemm_within_bound(c, C, B, out == "bf16", f"mid-size {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,out", [(128, "f32"), (96, "bf16")])
+def test_mid_m_full_size(M, out):
+    """M tokens against the decode workload's pre-quantized 18432 x 7168 weight; every output element is
+    checked."""
+    d = wl.decode()
+    g = np.random.default_rng([68, M])
+    ab = wl.bf16_bits(g.standard_normal((M, 7168)).astype(np.float32))
+    say(f"gemm: mid-size {M}x18432x7168 out={out}")
+    qa, sa = fq.fp8q_quant_act_1x128(bf16_dev(ab))
+    c = gemm_out_to_f64(fq.fp8q_gemm_blockscaled(qa, sa, u8_dev(d["wq"]), f32_dev(d["sw"]), out_dtype=DT[out]))
+    oqa, osa = oracle.quant_act_1x128(ab)
+    C, B = oracle.gemm_blockscaled(oqa, osa, d["wq"], d["sw"])
+    r = assert_gemm_within_bound(c, C, B, out == "bf16", "mid-size full")
+    say(f"  max err/bound {r:.3g}; literal-bound ratio {literal_bound_ratio(c, C, B):.3g}")
+
+
 # ------------------------------------------------------------------ grouped (MoE)
 
 def grouped_case(seed, counts, N, K):
