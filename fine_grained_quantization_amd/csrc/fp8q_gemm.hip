@@ -12,9 +12,9 @@
 //    s_a[kb][m] * s_w[n/128][kb], and stores 4 adjacent outputs with one instruction.
 //  * Operand tiles travel from global memory straight into LDS (buffer loads into LDS), rows stored
 //    with a 16-byte-chunk XOR swizzle so that fragment reads are bank-conflict free.
-// M > 128 runs the 256-row tile kernel (dense, grouped and gather-fused grouped); M <= 64 the small-M
-// kernel, whose waves split K; 64 < M <= 128 the mid-size kernel, whose waves split the tokens.  The
-// latter two give each CU one slice of weight rows, so the weights are streamed from HBM once.
+// M > 256 runs the 256-row tile kernel (as do the grouped and gather-fused grouped GEMMs); M <= 64 the
+// small-M kernel, whose waves split K; 64 < M <= 256 the mid-size kernel, whose waves split the tokens.
+// The latter two give each CU one slice of weight rows, so the weights are streamed from HBM once.
 
 #include <atomic>
 
@@ -785,35 +785,44 @@ __global__ __launch_bounds__(512, 1) void gemm_smallm_kernel(const uint8_t *__re
 }
 
 // =============================================================================================
-// Mid-size M kernel (64 < M <= 128): as in the small-M kernel, the N rows are dealt out in slices of R rows (one
-// slice per CU, R <= 80), so the weight matrix is streamed from HBM exactly once by all CUs; here every
-// workgroup holds all 128 token rows, and the 8 waves split the tokens instead of K: wave w owns token subtile w
-// (16 tokens) and all NSUB weight subtiles, so each output has one owner and no partial sums are exchanged.  The
-// K-blocks flow through a ring of kMidStages LDS stages shared by the waves: each stage holds a K-block's weight
-// rows, its 128 token rows and their scales, copied with buffer loads straight into LDS (rows past the slice or
-// past M read zeros), and the copies run kMidStages - 1 K-blocks ahead of the MFMAs.  Every wave issues the same
-// kMidCopies copy instructions per K-block, so the number of its loads still in flight is the same constant
-// every iteration: where a wave has nothing to copy, it loads through a zero-byte resource into a scratch area
-// of LDS that nothing reads (a load into LDS that is out of range still writes its zeros).
+// Mid-size M kernel (64 < M <= 256, MT = 128 or 256 token rows): as in the small-M kernel, the N rows are dealt
+// out in slices of R rows (one slice per CU, R <= 80), so the weight matrix is streamed from HBM exactly once by
+// all CUs; here every workgroup holds all MT token rows, and the 8 waves split the tokens instead of K: wave w
+// owns token subtiles w, w + 8, ... (MT / 128 of them) and all NSUB weight subtiles, so each output has one
+// owner and no partial sums are exchanged.  The K-blocks flow through a ring of LDS stages shared by the waves:
+// each stage holds a K-block's weight rows, its MT token rows and their scales, copied with buffer loads straight
+// into LDS (rows past the slice or past M read zeros), and the copies run (stages - 1) K-blocks ahead of the
+// MFMAs.  Every wave issues the same number of copy instructions per K-block, so the number of its loads still
+// in flight is the same constant every iteration: where a wave has nothing to copy, it loads through a
+// zero-byte resource into a scratch area of LDS that nothing reads (a load into LDS that is out of range still
+// writes its zeros).
 // =============================================================================================
 
-constexpr int kMidM = 128;
-constexpr int kMidStages = 5;  // 5 x (10 KB weight + 16 KB tokens + 768 B scales) + 1 KB = 135 KB of LDS
-constexpr int kMidCopies = 5;  // copy instructions per wave per K-block: 2 token groups, 2 weight groups, 1 scale
+template <int MT>
+struct MidShape {
+    static_assert(MT == 128 || MT == 256, "token rows per workgroup");
+    static constexpr int kTpw = MT / 128;                       // token subtiles per wave
+    static constexpr int kCopies = 2 * kTpw + 3;                // token groups, 2 weight groups, 1 scale dword
+    static constexpr int kStages = MT == 128 ? 5 : 3;           // 135 KB / 131 KB of LDS with 80-row slices
+};
 
-template <bool OUT_BF16, int NSUB>
+template <bool OUT_BF16, int NSUB, int MT>
 __global__ __launch_bounds__(512, 1) void gemm_midm_kernel(const uint8_t *__restrict__ qa,
                                                            const float *__restrict__ sa,
                                                            const uint8_t *__restrict__ qw,
                                                            const float *__restrict__ sw, void *__restrict__ c,
                                                            int64_t M, int64_t N, int64_t K, int64_t rows_per_wg) {
+    using MS = MidShape<MT>;
+    constexpr int S = MS::kStages;
+    constexpr int TPW = MS::kTpw;
     constexpr int kW = NSUB * 16 * 128;   // weight rows of one K-block
-    constexpr int kA = kMidM * 128;       // token rows of one K-block
-    constexpr int kSa = kW + kA;          // 128 token scales
-    constexpr int kSw = kSa + kMidM * 4;  // weight scales of blocks nb0, nb0 + 1 (64 slots)
+    constexpr int kA = MT * 128;          // token rows of one K-block
+    constexpr int kSa = kW + kA;          // MT token scales
+    constexpr int kSw = kSa + MT * 4;     // weight scales of blocks nb0, nb0 + 1 (64 slots)
     constexpr int kStage = kSw + 256;
-    constexpr int kDummy = kMidStages * kStage;  // 1 KB that absorbs the zeros of the loads with nothing to copy
+    constexpr int kDummy = S * kStage;    // 1 KB that absorbs the zeros of the loads with nothing to copy
     static_assert(2 * NSUB <= 16, "at most 16 weight row groups");
+    static_assert(kDummy + 1024 <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDummy + 1024];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -829,20 +838,25 @@ __global__ __launch_bounds__(512, 1) void gemm_midm_kernel(const uint8_t *__rest
     const i32x4 rSW = make_rsrc(sw, (uint64_t)(N / 128) * (uint64_t)KB * 4);
 
     // Copy assignment.  Row groups of 8 rows (1 KB, one instruction): lane l lands in row 8 j + l / 8, physical
-    // chunk l % 8, which holds logical chunk (l % 8) ^ swzf(row).  Wave w copies token groups w and w + 8, weight
-    // groups w and w + 8 (when they exist), and one scale dword per lane: waves 0 and 1 the token scales of
-    // tokens [64 w, 64 w + 64), wave 2 the weight scales of blocks nb0 and nb0 + 1 (lanes 0 and 1).
+    // chunk l % 8, which holds logical chunk (l % 8) ^ swzf(row).  Wave w copies token groups w, w + 8, ...
+    // (MT / 64 of them), weight groups w and w + 8 (when they exist), and one scale dword per lane: waves
+    // 0 .. MT / 64 - 1 the token scales of tokens [64 w, 64 w + 64), wave MT / 64 the weight scales of blocks nb0
+    // and nb0 + 1 (lanes 0 and 1).
+    constexpr int kTokWaves = MT / 64;
     const int rsub = lane >> 3;
-    int voff[2];  // rows 8 (w + 8 j) + l / 8 of either operand
+    int a_voff[2 * TPW], w_voff[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < 2 * TPW; j++) {
         const int r = 8 * (wave + 8 * j) + rsub;
-        voff[j] = r * (int)K + (((lane & 7) ^ swzf(r)) << 4);
+        a_voff[j] = r * (int)K + (((lane & 7) ^ swzf(r)) << 4);
     }
+#pragma unroll
+    for (int j = 0; j < 2; j++) w_voff[j] = a_voff[j];  // the same rows 8 (w + 8 j) + l / 8 of the weight slice
     const bool has_w0 = wave < 2 * NSUB, has_w1 = wave + 8 < 2 * NSUB;  // wave-uniform
+    const bool tok_sc = wave < kTokWaves, w_sc = wave == kTokWaves;
     const int64_t nbl = nb0 + lane < N / 128 - 1 ? nb0 + lane : N / 128 - 1;
-    const int sc_voff = wave < 2 ? (wave * 64 + lane) * 4 : (lane < 2 ? (int)(nbl * KB * 4) : kOutOfRange);
-    const int sc_lds = wave < 2 ? kSa + wave * 256 : kSw;
+    const int sc_voff = tok_sc ? (wave * 64 + lane) * 4 : (lane < 2 ? (int)(nbl * KB * 4) : kOutOfRange);
+    const int sc_lds = tok_sc ? kSa + wave * 256 : kSw;
     int sw_idx[NSUB];  // weight-scale slot (0 or 1) of this lane's 4 rows 16 ns + 4 (lane / 16) .. +3
 #pragma unroll
     for (int ns = 0; ns < NSUB; ns++) {
@@ -854,65 +868,76 @@ __global__ __launch_bounds__(512, 1) void gemm_midm_kernel(const uint8_t *__rest
     // Copies of K-block kb into its stage; past the last K-block (kb >= KB, wave-uniform) every resource has zero
     // bytes, so the loads read zeros without touching memory (and still count as issued loads).
     auto issue = [&](int kb) {
-        uint8_t *st = lds + (kb % kMidStages) * kStage;
+        uint8_t *st = lds + (kb % S) * kStage;
         const bool in = kb < KB;
         const int so = in ? kb * 128 : 0;
         const i32x4 ta = in ? rA : empty_rsrc(rA);
         const i32x4 tw0 = in && has_w0 ? rw : empty_rsrc(rw), tw1 = in && has_w1 ? rw : empty_rsrc(rw);
         // Token scales: the K-block's offset goes into the per-lane offset, which the hardware range-checks, so
         // tokens past M in the last K-block read zeros (the scalar offset is not range-checked).
-        const i32x4 ts = !in ? empty_rsrc(rS) : (wave < 2 ? rS : (wave == 2 ? rSW : empty_rsrc(rSW)));
-        const int svo = wave < 2 && in ? sc_voff + kb * (int)M * 4 : sc_voff;
-        const int sso = wave == 2 && in ? kb * 4 : 0;
-        fp8q_raw_buffer_load_lds(ta, (lds_ptr)(st + kW + wave * 1024), 16, voff[0], so, 0, 0);
-        fp8q_raw_buffer_load_lds(ta, (lds_ptr)(st + kW + (wave + 8) * 1024), 16, voff[1], so, 0, 0);
-        fp8q_raw_buffer_load_lds(tw0, (lds_ptr)(has_w0 ? st + wave * 1024 : lds + kDummy), 16, voff[0], so, 0, 0);
-        fp8q_raw_buffer_load_lds(tw1, (lds_ptr)(has_w1 ? st + (wave + 8) * 1024 : lds + kDummy), 16, voff[1], so, 0,
-                                 0);
-        fp8q_raw_buffer_load_lds(ts, (lds_ptr)(wave <= 2 ? st + sc_lds : lds + kDummy), 4, svo, sso, 0, 0);
+        const i32x4 ts = !in ? empty_rsrc(rS) : (tok_sc ? rS : (w_sc ? rSW : empty_rsrc(rSW)));
+        const int svo = tok_sc && in ? sc_voff + kb * (int)M * 4 : sc_voff;
+        const int sso = w_sc && in ? kb * 4 : 0;
+#pragma unroll
+        for (int j = 0; j < 2 * TPW; j++)
+            fp8q_raw_buffer_load_lds(ta, (lds_ptr)(st + kW + (wave + 8 * j) * 1024), 16, a_voff[j], so, 0, 0);
+        fp8q_raw_buffer_load_lds(tw0, (lds_ptr)(has_w0 ? st + wave * 1024 : lds + kDummy), 16, w_voff[0], so, 0, 0);
+        fp8q_raw_buffer_load_lds(tw1, (lds_ptr)(has_w1 ? st + (wave + 8) * 1024 : lds + kDummy), 16, w_voff[1], so,
+                                 0, 0);
+        fp8q_raw_buffer_load_lds(ts, (lds_ptr)(tok_sc || w_sc ? st + sc_lds : lds + kDummy), 4, svo, sso, 0, 0);
     };
 
-    v4f acc[NSUB];
+    v4f acc[TPW][NSUB];
 #pragma unroll
-    for (int ns = 0; ns < NSUB; ns++) acc[ns] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TPW; t++)
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ns++) acc[t][ns] = (v4f){0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int s = 0; s < kMidStages - 1; s++) issue(s);
+    for (int s = 0; s < S - 1; s++) issue(s);
     for (int kb = 0; kb < KB; kb++) {
-        // This wave's copies of K-block kb have landed (those of the next kMidStages - 2 may still be in flight);
-        // after the barrier every wave's have, and every wave is done with the stage K-block kb - 1 used.  (A
-        // plain s_barrier: __syncthreads would also wait for every load in flight.  The stage's data was written
-        // by the loads, and every read of the freed stage has returned, as its MFMAs and products consumed it.)
-        __builtin_amdgcn_s_waitcnt(vmcnt_le<(kMidStages - 2) * kMidCopies>());
+        // This wave's copies of K-block kb have landed (those of the next S - 2 may still be in flight); after
+        // the barrier every wave's have, and every wave is done with the stage K-block kb - 1 used.  (A plain
+        // s_barrier: __syncthreads would also wait for every load in flight.  The stage's data was written by the
+        // loads, and every read of the freed stage has returned, as its MFMAs and products consumed it.)
+        __builtin_amdgcn_s_waitcnt(vmcnt_le<(S - 2) * MS::kCopies>());
         __builtin_amdgcn_s_barrier();
-        issue(kb + kMidStages - 1);
-        const uint8_t *st = lds + (kb % kMidStages) * kStage;
+        issue(kb + S - 1);
+        const uint8_t *st = lds + (kb % S) * kStage;
         const float *ssc = reinterpret_cast<const float *>(st + kSa);
         const float *wsc = reinterpret_cast<const float *>(st + kSw);
-        const v8i af = load_frag(st + kW, wave * 16, lane);
-        v8i wf[NSUB];
+        v8i af[TPW], wf[NSUB];
+#pragma unroll
+        for (int t = 0; t < TPW; t++) af[t] = load_frag(st + kW, (wave + 8 * t) * 16, lane);
 #pragma unroll
         for (int ns = 0; ns < NSUB; ns++) wf[ns] = load_frag(st, ns * 16, lane);
-        const float s_tok = ssc[wave * 16 + (lane & 15)];
+        float s_tok[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; t++) s_tok[t] = ssc[(wave + 8 * t) * 16 + (lane & 15)];
         const float sw0 = wsc[0], sw1 = wsc[1];
 #pragma unroll
-        for (int ns = 0; ns < NSUB; ns++) {
-            const v4f p = mfma_fp8_16x16x128(wf[ns], af, zero);
-            const float cs = s_tok * (sw_idx[ns] ? sw1 : sw0);
+        for (int ns = 0; ns < NSUB; ns++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[ns][r] = __builtin_fmaf(p[r], cs, acc[ns][r]);
-        }
+            for (int t = 0; t < TPW; t++) {
+                const v4f p = mfma_fp8_16x16x128(wf[ns], af[t], zero);
+                const float cs = s_tok[t] * (sw_idx[ns] ? sw1 : sw0);
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[t][ns][r] = __builtin_fmaf(p[r], cs, acc[t][ns][r]);
+            }
     }
-    // Lane holds C[m][n .. n+3] of each subtile, m = 16 wave + lane % 16, n = 16 ns + 4 (lane / 16) within the
-    // slice; rows n are all in or all out of the slice.
+    // Lane holds C[m][n .. n+3] of each subtile, m = 16 (wave + 8 t) + lane % 16, n = 16 ns + 4 (lane / 16)
+    // within the slice; rows n are all in or all out of the slice.
     __builtin_amdgcn_s_waitcnt(0);  // the last (zero-byte) copies have retired before the workgroup ends
-    const int64_t m = wave * 16 + (lane & 15);
-    if (m < M) {
 #pragma unroll
-        for (int ns = 0; ns < NSUB; ns++) {
-            const int nl = ns * 16 + 4 * (lane >> 4);
-            if (nl < nrows) store4<OUT_BF16>(c, m * N + n0 + nl, acc[ns]);
+    for (int t = 0; t < TPW; t++) {
+        const int64_t m = (wave + 8 * t) * 16 + (lane & 15);
+        if (m < M) {
+#pragma unroll
+            for (int ns = 0; ns < NSUB; ns++) {
+                const int nl = ns * 16 + 4 * (lane >> 4);
+                if (nl < nrows) store4<OUT_BF16>(c, m * N + n0 + nl, acc[t][ns]);
+            }
         }
     }
 }
@@ -956,7 +981,7 @@ hipError_t launch_smallm(const uint8_t *qa, const float *sa, const uint8_t *qw, 
     return hipGetLastError();
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int MT>
 hipError_t launch_midm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw, void *c, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
     // The small-M kernel's slices: a multiple of 8 rows giving about one slice per CU, at most 5 subtiles.
@@ -968,7 +993,7 @@ hipError_t launch_midm(const uint8_t *qa, const float *sa, const uint8_t *qw, co
     switch (nsub) {
 #define FP8Q_MIDM_CASE(S)                                                                                  \
     case S:                                                                                                \
-        gemm_midm_kernel<OUT_BF16, S><<<grid, 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, rows);         \
+        gemm_midm_kernel<OUT_BF16, S, MT><<<grid, 512, 0, stream>>>(qa, sa, qw, sw, c, M, N, K, rows);     \
         break;
         FP8Q_MIDM_CASE(1)
         FP8Q_MIDM_CASE(2)
@@ -999,9 +1024,12 @@ hipError_t launch_gemm_blockscaled(const uint8_t *qa, const float *sa, const uin
     if (M <= kSmallM)
         return out_bf16 ? launch_smallm<true>(qa, sa, qw, sw, c, M, N, K, stream)
                         : launch_smallm<false>(qa, sa, qw, sw, c, M, N, K, stream);
-    if (M <= kMidM)
-        return out_bf16 ? launch_midm<true>(qa, sa, qw, sw, c, M, N, K, stream)
-                        : launch_midm<false>(qa, sa, qw, sw, c, M, N, K, stream);
+    if (M <= 128)
+        return out_bf16 ? launch_midm<true, 128>(qa, sa, qw, sw, c, M, N, K, stream)
+                        : launch_midm<false, 128>(qa, sa, qw, sw, c, M, N, K, stream);
+    if (M <= 256)
+        return out_bf16 ? launch_midm<true, 256>(qa, sa, qw, sw, c, M, N, K, stream)
+                        : launch_midm<false, 256>(qa, sa, qw, sw, c, M, N, K, stream);
     return out_bf16 ? launch_256<true>(qa, sa, qw, sw, c, M, N, K, stream)
                     : launch_256<false>(qa, sa, qw, sw, c, M, N, K, stream);
 }

@@ -256,13 +256,16 @@ def test_decode_small_m_full_size(out):
     say(f"  max err/bound {r:.3g}; literal-bound ratio {literal_bound_ratio(c, C, B):.3g}")
 
 
-# N -> slice rows as for the small-M kernel; the mid-size-M kernel (64 < M <= 128) takes every token row in one
-# workgroup: 256 -> 8 rows (NSUB 1), 4352 -> 24 (2), 8320 -> 40 (3), 12416 -> 56 (4), 18432 -> 72 (5).  K = 128
-# and 384 leave fewer K-blocks than the copies run ahead.
+# N -> slice rows as for the small-M kernel; the mid-size-M kernel (64 < M <= 256) takes every token row in one
+# workgroup (128 or 256 of them): 256 -> 8 rows (NSUB 1), 4352 -> 24 (2), 8320 -> 40 (3), 12416 -> 56 (4),
+# 18432 -> 72 (5).  K = 128, 256 and 384 leave fewer K-blocks than the copies run ahead.
 @pytest.mark.parametrize("M,N,K,out", [(65, 256, 384, "f32"), (128, 4352, 384, "bf16"), (96, 8320, 128, "f32"),
-                                       (100, 12416, 384, "bf16"), (127, 18432, 640, "f32"), (128, 18432, 256, "bf16")])
+                                       (100, 12416, 384, "bf16"), (127, 18432, 640, "f32"), (128, 18432, 256, "bf16"),
+                                       (129, 256, 128, "bf16"), (256, 4352, 640, "f32"), (200, 8320, 256, "bf16"),
+                                       (255, 12416, 384, "f32"), (192, 18432, 512, "bf16")])
 def test_mid_m_slice_widths(M, N, K, out):
-    """Every subtile count of the mid-size-M kernel, ragged token counts and short K."""
+    """Every subtile count of the mid-size-M kernel for both token-row counts, ragged token counts and short
+    K."""
     g = np.random.default_rng([67, M, N, K])
     a = g.standard_normal((M, K)).astype(np.float32)
     a *= np.exp2(g.integers(-6, 7, size=(M, 1))).astype(np.float32)
@@ -274,7 +277,7 @@ def test_mid_m_slice_widths(M, N, K, out):
     assert_gemm_within_bound(c, C, B, out == "bf16", f"mid-size {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,out", [(128, "f32"), (96, "bf16")])
+@pytest.mark.parametrize("M,out", [(128, "f32"), (96, "bf16"), (256, "bf16"), (160, "f32")])
 def test_mid_m_full_size(M, out):
     """M tokens against the decode workload's pre-quantized 18432 x 7168 weight; every output element is
     checked."""
