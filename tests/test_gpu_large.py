@@ -122,10 +122,10 @@ def test_gemm_activation_past_4gib(out):
     say(f"  max err/bound {ratio:.3g}")
 
 
-@pytest.mark.parametrize("M", [256, 64])
+@pytest.mark.parametrize("M", [512, 256, 64])
 def test_gemm_weight_past_4gib(M):
-    """W [600064, 7168] codes (4.0 GiB) with M = 256 (large-M kernel) and M = 64 (small-M kernel): the
-    128-row weight blocks on both sides of the 2^32-byte boundary and the last one."""
+    """W [600064, 7168] codes (4.0 GiB) with M = 512 (large-M kernel), M = 256 (mid-size-M kernel) and M = 64
+    (small-M kernel): the 128-row weight blocks on both sides of the 2^32-byte boundary and the last one."""
     qa, sa = e4m3_codes(M, 110), scales((K // 128, M), 111)
     qw, sw = e4m3_codes(BIG, 112), scales((BIG // 128, K // 128), 113)
     say(f"large: gemm A [{M}, {K}] x W [{BIG}, {K}]")
@@ -214,7 +214,8 @@ def codes_k(rows, k, seed):
     return (r + (r >= 127).to(torch.int16)).to(torch.uint8)
 
 
-@pytest.mark.parametrize("M", [300, 64])   # the large-M kernel (a whole and a partial M tile) and small-M
+# the large-M kernel (a whole and a partial M tile), the mid-size-M kernel (256 and 128 token rows), small-M
+@pytest.mark.parametrize("M", [300, 256, 100, 64])
 def test_gemm_at_the_largest_k(M):
     """K = 2^23 (65,536 K-blocks): the last row of a 256-row tile starts 255 * 2^23 bytes into it, so the
     per-lane buffer offsets reach 2^31 - 16.  Sampled rows (both ends of each M tile) x sampled columns of
