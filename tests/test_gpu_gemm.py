@@ -168,8 +168,9 @@ def test_deterministic():
 
 
 def test_repeat_calls_give_the_same_bits():
-    """The small-M kernel (partial sums of 8 waves added in wave order), the grouped kernel and its
-    gather-fused form give bit-identical outputs on repeated calls, as the dense kernel does."""
+    """The small-M kernel (partial sums of 8 waves added in wave order), the mid-size-M kernel (its stage ring,
+    128 and 256 token rows), the grouped kernel and its gather-fused form give bit-identical outputs on
+    repeated calls, as the dense kernel does."""
     g = np.random.default_rng(9)
     K, N = 1024, 2048
     q = g.integers(0, 254, size=(300, K)).astype(np.uint8)
@@ -179,13 +180,15 @@ def test_repeat_calls_give_the_same_bits():
     qw, sw = fq.fp8q_quant_w_128x128(bf16_dev(w).view(4, N, K))
     qd, sd = u8_dev(q), f32_dev(s)
     small = [host(fq.fp8q_gemm_blockscaled(qd[:48], sd[:, :48].contiguous(), qw[0], sw[0])) for _ in range(3)]
+    mid = [host(fq.fp8q_gemm_blockscaled(qd[:m], sd[:, :m].contiguous(), qw[1], sw[1], out_dtype=torch.float32))
+           for m in (100, 100, 100, 200, 200, 200)]
     off = torch.tensor([0, 128, 128, 256, 256], dtype=torch.int32, device="cuda")
     grouped = [host(fq.fp8q_grouped_gemm_blockscaled(qd[:256], sd[:, :256].contiguous(), qw, sw, off))
                for _ in range(3)]
     rt = torch.from_numpy(g.integers(-1, 300, size=256).astype(np.int32)).cuda()
     gathered = [host(fq.fp8q_grouped_gemm_blockscaled_gather(qd, sd, rt, qw, sw, off, out_dtype=torch.float32))
                 for _ in range(3)]
-    for runs in (small, grouped, gathered):
+    for runs in (small, mid[:3], mid[3:], grouped, gathered):
         for r in runs[1:]:
             assert np.array_equal(r.view(np.uint8), runs[0].view(np.uint8))
 

@@ -1,7 +1,8 @@
 """HIP graph capture of the library's calls.  Each step the benchmark times, at a small size, is captured once
 into a graph (torch.cuda.CUDAGraph) and replayed several times: the dense step (quantize A, quantize W, GEMM),
-the decode step (quantize 64 tokens, small-M GEMM) and the MoE step (token quantization and routing on a second
-stream beside the weight quantization, then the grouped GEMM reading the routed token rows).  Between replays
+the decode step (quantize 64 tokens, small-M GEMM), the same at 96 and 200 tokens (mid-size-M GEMM) and the
+MoE step (token quantization and routing on a second stream beside the weight quantization, then the grouped
+GEMM reading the routed token rows).  Between replays
 the inputs are rewritten by eager work and every output is overwritten with a sentinel, then the stream is
 synchronized; each replay's outputs must equal those of the same calls made eagerly on the same inputs.  The
 library records no memset, allocation or synchronization, so a graph holds its kernel launches only."""
@@ -98,6 +99,25 @@ def test_decode_step_in_a_graph():
         fq.fp8q_gemm_blockscaled(qa, sa, qw, sw, out_dtype=torch.float32, c=c)
 
     check_replays("decode step", capture(step), step, lambda: x.copy_(bf((M, K), g)), [qa, sa, c])
+
+
+@pytest.mark.parametrize("M", [96, 200])
+def test_mid_size_step_in_a_graph(M):
+    """The decode step at 96 and 200 tokens (the mid-size-M kernel, 128 and 256 token rows per workgroup)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23 + M)
+    N, K = 2048, 1024
+    x = bf((M, K), g)
+    qw, sw = fq.fp8q_quant_w_128x128(bf((N, K), g, 0.02))
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        fq.fp8q_quant_act_1x128(x, qa, sa)
+        fq.fp8q_gemm_blockscaled(qa, sa, qw, sw, c=c)
+
+    check_replays(f"mid-size step, M = {M}", capture(step), step, lambda: x.copy_(bf((M, K), g)), [qa, sa, c])
 
 
 def test_moe_step_on_two_streams_in_a_graph():
