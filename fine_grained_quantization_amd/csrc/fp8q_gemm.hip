@@ -344,56 +344,8 @@ __device__ __forceinline__ void bs_tile(uint8_t *stage0, uint8_t *stage1, const 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
     // The K-loop.  Waves with a subtile without a live bit take a partial form that skips that subtile's
-    // fragment reads, MFMAs and promotions; full waves run the loop below (a macro, expanded once) without any
-    // branch.  Both forms reach the same barriers.  Per K-block: wait for this K-block's tiles (own loads) and
-    // for every wave to be done with the other stage; prefetch the next K-block (unconditionally: past the last
-    // K-block it copies no tiles); read the first weight fragment before the activation fragments, so that the
-    // first MFMA waits for two LDS reads, not five; read weight subtile ni+1's fragment while subtile ni's 4
-    // MFMAs run, and promote their partials right after issue.
-#define FP8Q_BS_KLOOP()                                                                                   \
-    for (int64_t kb = 0; kb < KB; kb++) {                                                                        \
-        uint8_t *cur = (kb & 1) ? stage1 : stage0;                                                               \
-        uint8_t *nxt = (kb & 1) ? stage0 : stage1;                                                               \
-        __builtin_amdgcn_s_waitcnt(0);                                                                           \
-        __syncthreads();                                                                                         \
-        ld.issue(nxt, kb + 1 < KB, (int)((kb + 1) * 128), kb + 1 < KB ? kb + 1 : kb, wave);                      \
-        const uint8_t *tW = cur + kBig * 128;                                                                    \
-        v8i wf = load_frag(tW, wn * WN, lane);                                                                   \
-        v8i af[4];                                                                                               \
-_Pragma("unroll")                                                                                                \
-        for (int mi = 0; mi < 4; mi++)                                                                           \
-            af[mi] = load_frag(cur, wm * 64 + mi * 16, lane);                                                    \
-        const float *sc = reinterpret_cast<const float *>(cur + TileLoader<BN>::kScOff);                         \
-        float sa_cur[4], csA[4];                                                                                 \
-_Pragma("unroll")                                                                                                \
-        for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sc[wm * 64 + mi * 16 + (lane & 15)];                         \
-        const float swA = sc[256 + nbA], swB = sc[256 + nbB];                                                    \
-_Pragma("unroll")                                                                                                \
-        for (int mi = 0; mi < 4; mi++) csA[mi] = sa_cur[mi] * swA;                                               \
-_Pragma("unroll")                                                                                                \
-        for (int ni = 0; ni < NSUB; ni++) {                                                                      \
-            v8i wf_next = wf;                                                                                    \
-            if (ni < NSUB - 1) wf_next = load_frag(tW, wn * WN + (ni + 1) * 16, lane);                           \
-            v4f p[4];                                                                                            \
-_Pragma("unroll")                                                                                                \
-            for (int mi = 0; mi < 4; mi++)                                                                       \
-                p[mi] = mfma_fp8_16x16x128(wf, af[mi], zero);                                                    \
-            float cs[4];                                                                                         \
-            if (NSUB == 8) {                                                                                     \
-_Pragma("unroll")                                                                                                \
-                for (int mi = 0; mi < 4; mi++) cs[mi] = csA[mi];                                                 \
-            } else {                                                                                             \
-                const float swv = ni < nib ? swA : swB;                                                          \
-_Pragma("unroll")                                                                                                \
-                for (int mi = 0; mi < 4; mi++) cs[mi] = sa_cur[mi] * swv;                                        \
-            }                                                                                                    \
-_Pragma("unroll")                                                                                                \
-            for (int mi = 0; mi < 4; mi++)                                                                       \
-_Pragma("unroll")                                                                                                \
-                for (int r = 0; r < 4; r++) acc[ni][mi][r] = __builtin_fmaf(p[mi][r], cs[mi], acc[ni][mi][r]);   \
-            wf = wf_next;                                                                                        \
-        }                                                                                                        \
-    }
+    // fragment reads, MFMAs and promotions; full waves run the second loop, which has no branch in its body.
+    // Both forms reach the same barriers.
     if (GATHER && live != 0xFu) {
         // The partial form: all weight fragments of the K-block are read first, then each live token subtile
         // runs its MFMAs and promotions against them (one wave-uniform test per subtile and K-block).
@@ -424,9 +376,56 @@ _Pragma("unroll")                                                               
             }
         }
     } else {
-        FP8Q_BS_KLOOP()
+        for (int64_t kb = 0; kb < KB; kb++) {
+            uint8_t *cur = (kb & 1) ? stage1 : stage0;
+            uint8_t *nxt = (kb & 1) ? stage0 : stage1;
+            // This K-block's tiles have landed (own loads), and every wave is done with the other stage.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            // The prefetch is unconditional (past the last K-block it copies no tiles and yields zeros), so
+            // the loop body is a single basic block.
+            ld.issue(nxt, kb + 1 < KB, (int)((kb + 1) * 128), kb + 1 < KB ? kb + 1 : kb, wave);
+            // The first weight fragment is read before the activation fragments so that the first MFMA waits
+            // for two LDS reads, not five.  The fragment of weight subtile ni+1 is read while the 4 MFMAs of
+            // subtile ni run; their partials are promoted right after issue (the first MFMA has finished by
+            // the time the 4th issues).
+            const uint8_t *tW = cur + kBig * 128;
+            v8i wf = load_frag(tW, wn * WN, lane);
+            v8i af[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; mi++) af[mi] = load_frag(cur, wm * 64 + mi * 16, lane);
+            // Scales (needed from the first promotion on) of tokens wm * 64 + mi * 16 + (lane & 15).
+            const float *sc = reinterpret_cast<const float *>(cur + TileLoader<BN>::kScOff);
+            float sa_cur[4], csA[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; mi++) sa_cur[mi] = sc[wm * 64 + mi * 16 + (lane & 15)];
+            const float swA = sc[256 + nbA], swB = sc[256 + nbB];
+#pragma unroll
+            for (int mi = 0; mi < 4; mi++) csA[mi] = sa_cur[mi] * swA;
+#pragma unroll
+            for (int ni = 0; ni < NSUB; ni++) {
+                v8i wf_next = wf;
+                if (ni < NSUB - 1) wf_next = load_frag(tW, wn * WN + (ni + 1) * 16, lane);
+                v4f p[4];
+#pragma unroll
+                for (int mi = 0; mi < 4; mi++) p[mi] = mfma_fp8_16x16x128(wf, af[mi], zero);
+                float cs[4];
+                if (NSUB == 8) {
+#pragma unroll
+                    for (int mi = 0; mi < 4; mi++) cs[mi] = csA[mi];
+                } else {
+                    const float swv = ni < nib ? swA : swB;  // scalar select
+#pragma unroll
+                    for (int mi = 0; mi < 4; mi++) cs[mi] = sa_cur[mi] * swv;
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[ni][mi][r] = __builtin_fmaf(p[mi][r], cs[mi], acc[ni][mi][r]);
+                wf = wf_next;
+            }
+        }
     }
-#undef FP8Q_BS_KLOOP
 
     // Epilogue: lane holds C[m][n .. n+3] of each subtile; rows outside [m0, mend) are not stored.
     if constexpr (OUT_BF16) {
